@@ -1,0 +1,30 @@
+"""CPU fp64 oracle for causal prefill attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in the repository's entry module and the
+CPU-baseline leg of the benchmark may import this package.  The product path
+(the HIP library and its Python binding) never imports, calls or links it, and
+this package shares no code with that path: it is a plain, slow restatement of
+what the path computes, written from the method's description, so that the
+GPU results can be checked against it.
+
+Contents
+--------
+formats    -- exact decoders for bf16 and OCP e4m3fn codes, a round-to-nearest-
+              even saturating e4m3 encoder, and absmax quantisation.
+attention  -- the plain definition of causal softmax attention in float64
+              (whole-row softmax, no online/tiled evaluation), over all rows or
+              over sampled (b, h, i) rows.
+
+Every function is pinned by the `-m "not gpu"` tests against library routines
+(torch's float8/bfloat16 casts, torch's scaled_dot_product_attention in fp64),
+closed forms (equal scores, row 0, hard-max limit), invariants (causality,
+rows of P summing to one, GQA == repeated-KV MHA) and brute-force loops on tiny
+inputs.  No function here is "parity unpinned".
+"""
+from .formats import (bf16_decode, e4m3_decode, e4m3_encode, quantize_e4m3,
+                      E4M3_MAX)
+from .attention import (causal_attention, causal_attention_rows, kv_head_of,
+                        visible_keys)
+
+__all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "E4M3_MAX",
+           "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys"]

@@ -1,0 +1,105 @@
+"""Number formats for the oracle (test infrastructure only).
+
+bf16: 1 sign, 8 exponent, 7 mantissa bits; a bf16 code is the upper half of
+the float32 with the same value (the BF16 description on kongchang.com, "ZYFA
+的性能与精度数据": 8 exponent and 7 mantissa bits).
+
+e4m3: 1 sign, 4 exponent, 3 mantissa bits (same section).  The variant is OCP
+E4M3FN (exponent bias 7, no infinities, codes 0x7F/0xFF are NaN, largest
+finite value 448 = code 0x7E), the variant gfx950's matrix instructions
+consume.  Read as an integer, the code of a power of two grows by 8 per
+doubling (the-ai.news "Drie technieken om de bottleneck te omzeilen";
+spke.com "Lean P"), which the tests pin.
+
+Quantisation maps each tensor (or each head) into the e4m3 range with one
+scale factor, accumulation staying in higher precision (kongchang.com "ZYFA
+的性能与精度数据": per-tensor or per-head scaling factors).  The reading used
+here: descale = absmax / 448 computed in float32, code = round-to-nearest-even
+of the float32 quotient x / descale, saturating at +-448.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_BIAS = 7
+_MIN_NORMAL_EXP = 1 - E4M3_BIAS          # -6
+_MANT_BITS = 3
+
+
+def bf16_decode(u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    u16 = np.asarray(u16, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn codes (uint8) -> exact float64 values (NaN for 0x7F/0xFF).
+
+    Field decoding: exponent field e, mantissa field m;
+    e == 0: subnormal, value = m * 2^(1 - bias - 3);  else (1 + m/8) * 2^(e - bias).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sub = m.astype(np.float64) * 2.0 ** (_MIN_NORMAL_EXP - _MANT_BITS)
+    nrm = (1.0 + m / 8.0) * np.exp2((e - E4M3_BIAS).astype(np.float64))
+    val = sign * np.where(e == 0, sub, nrm)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3fn codes, round to nearest (ties to even),
+    saturating finite overflow to +-448; NaN -> 0x7F.
+
+    Works on the value, not the bit pattern: find the binade 2^e of |x|
+    (clamped to the smallest normal binade 2^-6, below which the spacing is
+    the subnormal step 2^-9), round |x| / spacing to the nearest integer with
+    ties to even, rescale, clamp at 448, then write the fields.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    finite = np.isfinite(a)
+    a_f = np.where(finite, a, 0.0)
+    _, ex = np.frexp(a_f)                      # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, _MIN_NORMAL_EXP)    # binade exponent, clamped
+    spacing = np.exp2((e - _MANT_BITS).astype(np.float64))
+    r = np.rint(a_f / spacing) * spacing       # np.rint rounds half to even
+    r = np.minimum(r, E4M3_MAX)
+    r = np.where(np.isinf(a), E4M3_MAX, r)
+    # fields of the rounded value
+    _, er = np.frexp(np.where(r > 0, r, 1.0))
+    er = er - 1
+    is_sub = r < 2.0 ** _MIN_NORMAL_EXP
+    sub_code = np.rint(r / 2.0 ** (_MIN_NORMAL_EXP - _MANT_BITS))
+    mant = np.rint((r / np.exp2(er.astype(np.float64)) - 1.0) * 8.0)
+    nrm_code = (er + E4M3_BIAS) * 8 + mant
+    code = np.where(is_sub, sub_code, nrm_code).astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_e4m3(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, np.ndarray]:
+    """Absmax quantisation of a (B, N, H, d) float32 tensor.
+
+    Returns (codes uint8 (B,N,H,d), descale float32 of shape (H,) if per_head
+    else (1,)).  descale = float32(absmax) / float32(448) (float32 division);
+    an all-zero tensor/head gets descale 1.  Each code is the e4m3 rounding of
+    the float32 quotient x / descale, so code * descale reproduces x to within
+    e4m3's half-spacing.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 4:
+        raise ValueError("expected (B, N, H, d)")
+    if per_head:
+        amax = np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
+    else:
+        amax = np.array([np.max(np.abs(x))], dtype=np.float32)
+    descale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    descale = np.where(amax > 0, descale, np.float32(1.0)).astype(np.float32)
+    ds = descale[None, None, :, None] if per_head else descale[0]
+    qv = (x / ds).astype(np.float32)   # float32 / float32: correctly rounded
+    return e4m3_encode(qv), descale

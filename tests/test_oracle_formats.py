@@ -1,0 +1,123 @@
+"""bf16/e4m3 codecs and absmax quantisation of the oracle (CPU only).
+
+Pinned against torch's float8_e4m3fn and bfloat16 casts (library routines)
+and against the pages' "+8 per doubling" fact (tests/golden)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2 and set(codes[nan]) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def _midpoints_and_neighbours():
+    vals = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))      # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2                                  # exact in fp32
+    m32 = mids.astype(np.float32)
+    up = np.nextafter(m32, np.float32(np.inf))
+    dn = np.nextafter(m32, np.float32(0))
+    pts = np.concatenate([vals.astype(np.float32), m32, up, dn])
+    return np.concatenate([pts, -pts])
+
+
+def test_e4m3_encode_matches_torch_below_overflow():
+    rng = np.random.default_rng(0)
+    rnd = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * s for s in (1e-3, 0.05, 1, 30, 200)])
+    x = np.concatenate([_midpoints_and_neighbours(), rnd, np.float32([0.0, -0.0, 463.99, -463.99])])
+    x = x[np.abs(x) < 464]
+    assert np.array_equal(oracle.e4m3_encode(x), _torch_e4m3(x))
+
+
+def test_e4m3_encode_saturates():
+    x = np.float32([448, 449, 463.9, 464, 480, 1e4, 3e38, np.inf])
+    assert np.all(oracle.e4m3_encode(x) == 0x7E)
+    assert np.all(oracle.e4m3_encode(-x) == 0xFE)
+    assert oracle.e4m3_encode(np.float32([np.nan]))[0] == 0x7F
+
+
+def test_e4m3_roundtrip_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def test_e4m3_powers_of_two_golden():
+    """code(2^x) = 8x + 56 over the normal range: +8 per doubling."""
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_powers_of_two.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                x, val, code = line.split()
+                rows.append((int(x), float(val), int(code, 16)))
+    assert len(rows) == 18
+    for x, val, code in rows:
+        assert val == 2.0 ** x
+        assert oracle.e4m3_encode(np.float32([val]))[0] == code
+        assert oracle.e4m3_decode(np.uint8([code]))[0] == val
+        if x >= -6:
+            assert code == 8 * x + 56
+    normal = [c for x, _, c in rows if x >= -6]
+    assert all(b - a == 8 for a, b in zip(normal, normal[1:]))
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(1)
+    u = rng.integers(0, 2 ** 16, size=100000, dtype=np.uint16)
+    ref = torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_decode(u)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_matches_torch_cast_of_quotient(per_head):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 33, 3, 128)).astype(np.float32)
+    x[:, :, 1] *= 7.0
+    codes, ds = oracle.quantize_e4m3(x, per_head)
+    amax = np.abs(x).max(axis=(0, 1, 3)) if per_head else np.array([np.abs(x).max()])
+    assert ds.dtype == np.float32 and ds.shape == amax.shape
+    assert np.array_equal(ds, (amax.astype(np.float32) / np.float32(448)).astype(np.float32))
+    t = torch.from_numpy(x) / torch.from_numpy(ds[None, None, :, None] if per_head else ds)
+    ref = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    # the absmax element of each head (tensor) maps to +-448 exactly
+    for h in range(3):
+        sl = x[:, :, h] if per_head else x
+        c = codes[:, :, h] if per_head else codes
+        idx = np.unravel_index(np.argmax(np.abs(sl)), sl.shape)
+        assert c[idx] & 0x7F == 0x7E
+
+
+def test_quantize_error_bound_and_zero_tensor():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, 64, 2, 128)).astype(np.float32)
+    codes, ds = oracle.quantize_e4m3(x, True)
+    back = oracle.e4m3_decode(codes) * ds[None, None, :, None]
+    # half an e4m3 spacing: relative 2^-4 for normals, absolute 2^-10 * descale below
+    tol = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * ds[None, None, :, None]) * 1.0001
+    assert np.all(np.abs(back - x) <= tol)
+    z = np.zeros((1, 4, 2, 8), np.float32)
+    zc, zd = oracle.quantize_e4m3(z, True)
+    assert np.all(zc == 0) and np.all(zd == 1.0)

@@ -1,0 +1,116 @@
+// C-ABI entry points of libattn: argument validation, then launches on the caller's
+// stream.  Every check that can fail runs before the first HIP call, so invalid
+// arguments are reported without touching a device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 31;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_shape(int B, int Hq, int Hkv, int N, int d_qk, int d_v, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return ATTN_E_INVAL;
+  if (Hq % Hkv != 0) return ATTN_E_INVAL;
+  if (!(isfinite(scale) && scale > 0.f)) return ATTN_E_INVAL;
+  if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ATTN_E_UNSUPPORTED;
+  const long long bn = (long long)B * N;
+  if (bn * Hq * d_qk >= kMaxElems || bn * Hq * d_v >= kMaxElems) return ATTN_E_INVAL;
+  return ATTN_OK;
+}
+
+int check_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse) {
+  if (!q || !k || !v || !o) return ATTN_E_INVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_E_ALIGN;
+  if (lse && !aligned(lse, 4)) return ATTN_E_ALIGN;
+  return ATTN_OK;
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return ATTN_E_NODEVICE;
+  }
+  return ATTN_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                         float softmax_scale, void* stream) {
+  int st = check_shape(B, Hq, Hkv, N, d_qk, d_v, softmax_scale);
+  if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
+  if (st == ATTN_OK) st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.scale = softmax_scale;
+  return launch_status(attn::launch_attn_fwd(p, false, d_qk, (hipStream_t)stream));
+}
+
+int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                        const float* q_descale, const float* k_descale,
+                        const float* v_descale, int descale_per_head, void* o, float* lse,
+                        int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                        float softmax_scale, void* stream) {
+  int st = check_shape(B, Hq, Hkv, N, d_qk, d_v, softmax_scale);
+  if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
+  if (st == ATTN_OK && (!q_descale || !k_descale || !v_descale)) st = ATTN_E_INVAL;
+  if (st == ATTN_OK && (descale_per_head != 0 && descale_per_head != 1)) st = ATTN_E_INVAL;
+  if (st == ATTN_OK && (!aligned(q_descale, 4) || !aligned(k_descale, 4) ||
+                        !aligned(v_descale, 4)))
+    st = ATTN_E_ALIGN;
+  if (st == ATTN_OK) st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.scale = softmax_scale;
+  return launch_status(attn::launch_attn_fwd(p, true, d_qk, (hipStream_t)stream));
+}
+
+int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, int H, int d,
+                  int per_head, void* stream) {
+  if (!x || !out || !descale) return ATTN_E_INVAL;
+  if (B < 1 || N < 1 || H < 1 || d < 4 || (d & 3) != 0) return ATTN_E_INVAL;
+  if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
+  if (H > 65535) return ATTN_E_INVAL;
+  if ((long long)B * N * H * d >= kMaxElems) return ATTN_E_INVAL;
+  if (!aligned(x, 16) || !aligned(out, 4) || !aligned(descale, 4)) return ATTN_E_ALIGN;
+  const int st = check_device();
+  if (st != ATTN_OK) return st;
+  return launch_status(
+      attn::launch_quantize_e4m3(x, out, descale, B, N, H, d, per_head, (hipStream_t)stream));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVAL: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported head dims (need d_qk/d_v 128/128 or 192/128)";
+    case ATTN_E_ALIGN: return "misaligned tensor pointer";
+    case ATTN_E_NODEVICE: return "no usable HIP device";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,532 @@
+// Causal forward (prefill) attention kernels for gfx950 (CDNA4), BF16 and FP8 e4m3.
+//
+// What is computed: O = softmax(mask(Q K^T * scale)) V per (batch, query head), with
+// the query head h reading KV head h / (Hq / Hkv), and the log-sum-exp of each row.
+// The whole-row softmax is evaluated tile by tile with an online (running-max)
+// softmax so the score matrix never leaves registers (kongchang.com,
+// "为什么 prefill attention 值得单独优化").
+//
+// Formulation.  Each wave owns QT x 32 queries.  For a tile of 64 keys it forms the
+// TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs (A = K rows from LDS, B = Q^T held in
+// registers for the whole loop), so that in the 32x32 accumulator a lane holds one
+// query column and 16 keys of it: the row max, the exponentials and the row sums are
+// per-lane work plus one exchange with the lane 32 apart.  The second product is also
+// transposed, O^T = V^T P^T: the B operand P^T needs, per lane, probabilities of its
+// own query, which are exactly the values the lane already holds, so P goes from the
+// score accumulator to the MFMA operand without any cross-lane movement.  The keys a
+// lane holds are not contiguous (rows 8*(i/4) + 4*(lane/32) + i%4 of the accumulator),
+// so V is written to LDS transposed (V^T, one row per head-dim channel) with the keys
+// of each row permuted so that the 8 (bf16) or 32 (fp8) keys a lane needs for one MFMA
+// are contiguous: the contraction over keys does not care about key order as long as
+// both operands use the same one.
+//
+// FP8 probabilities (the-ai.news "Drie technieken om de bottleneck te omzeilen";
+// spke.com "Lean P" and "ブロックごとのスケーリングと丸められた行和"): the e4m3 code of
+// 2^y is 8y + 56 exactly at integer y and in between linear in y, so a probability
+// 2^(x + k) is written as the integer conversion of one FMA, s * 8c + (8k + C0 - 8c m).
+// k is a per-query, per-64-key-block power of two chosen so that the block maximum lands
+// in (2^7, 2^8] (codes <= 0x78) and small probabilities stay in the normal range; the
+// scaled MFMA's E8M0 operand scale 2^-k undoes it at no cost.  O is divided by the sum of
+// the same rounded probabilities, taken with one extra MFMA per block against a matrix
+// of ones, so the approximation's bias cancels in the normalisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BN = 64;     // keys per tile; also the FP8 probability scaling block
+constexpr int DV = 128;    // value head dim (both supported shapes)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+// Offset of the FP8 probability code: code = 8 * log2(p) + C0 before the integer
+// conversion, which rounds to nearest; 56 - 0.5 makes it act as truncation of
+// 8*log2(p) + 56, which keeps the piecewise-linear code close to unbiased.
+constexpr float LEANP_C0 = 55.5f;
+
+template <bool FP8, int DQK, int NW, int QT>
+struct Cfg {
+  static constexpr int EB = FP8 ? 1 : 2;            // bytes per element
+  static constexpr int NT = NW * 64;                 // threads per workgroup
+  static constexpr int BM = NW * QT * 32;            // queries per workgroup
+  static constexpr int KRB = DQK * EB;               // K row bytes
+  static constexpr int KROW = KRB + 16;              // padded LDS row (bank spread)
+  static constexpr int R16 = KRB / 16;               // 16-byte chunks per K row
+  static constexpr int KCH = BN * R16;               // chunks per K tile
+  static constexpr int KPT = (KCH + NT - 1) / NT;    // K chunks per thread
+  static constexpr int VROW = BN * EB + 16;          // padded LDS row of V^T
+  static constexpr int VUN = (BN / 4) * (DV / 8);    // units of 4 keys x 8 channels
+  static constexpr int VPT = (VUN + NT - 1) / NT;
+  static constexpr int K_BYTES = BN * KROW;
+  static constexpr int V_BYTES = DV * VROW;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int LDS = 2 * STAGE;              // double buffered
+  static constexpr int KS = FP8 ? DQK / 64 : DQK / 16;  // MFMA k-steps of Q K^T
+};
+
+// Position of key `k` (0..63) inside a V^T row of the LDS tile: the keys one lane
+// feeds to one P V MFMA become contiguous (see the file comment).
+template <bool FP8>
+__device__ __forceinline__ int vpos_of_group(int kg) {   // kg = key / 4
+  if (FP8) {  // key = 32m + 8a + 4g + b  ->  32g + 16m + 4a + b
+    return 32 * (kg & 1) + 16 * (kg >> 3) + 4 * ((kg >> 1) & 3);
+  } else {    // key = 16s + 8a + 4g + b  ->  16s + 8g + 4a + b
+    return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+  }
+}
+
+// Maps the flat workgroup id to (batch, query head, query tile).  Heaviest causal
+// tiles (last query rows) go first.  When B*Hkv is a multiple of 8, each of the 8
+// XCDs (workgroups are dealt to XCDs round-robin) gets whole KV-head groups, so the
+// query heads that share K/V run on one XCD and share its L2.
+__device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
+                                          int& qt) {
+  const int G = p.Hq / p.Hkv;
+  const int BHkv = p.B * p.Hkv;
+  if ((BHkv & 7) == 0) {
+    const int xcd = bid & 7, local = bid >> 3;
+    const int per = (BHkv >> 3) * G;
+    const int t = local / per, r = local - t * per;
+    qt = p.n_qtiles - 1 - t;
+    const int og = r / G, hg = r - og * G;
+    const int bk = xcd + 8 * og;
+    b = bk / p.Hkv;
+    h = (bk - b * p.Hkv) * G + hg;
+  } else {
+    const int per = p.B * p.Hq;
+    const int t = bid / per, r = bid - t * per;
+    qt = p.n_qtiles - 1 - t;
+    b = r / p.Hq;
+    h = r - b * p.Hq;
+  }
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+template <bool FP8, int DQK, int NW, int QT, bool WANT_LSE>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
+  using C = Cfg<FP8, DQK, NW, QT>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  int b, h, qt;
+  map_block(blockIdx.x, p, b, h, qt);
+  const int hkv = h / (p.Hq / p.Hkv);
+  const int N = p.N;
+  const int q0 = qt * C::BM;
+  const int q0w = q0 + wave * QT * 32;
+
+  const size_t kstride = (size_t)p.Hkv * DQK * C::EB;   // bytes between keys
+  const size_t vstride = (size_t)p.Hkv * DV * C::EB;
+  const char* kbase = (const char*)p.k + ((size_t)b * N * p.Hkv + hkv) * DQK * C::EB;
+  const char* vbase = (const char*)p.v + ((size_t)b * N * p.Hkv + hkv) * DV * C::EB;
+
+  // Softmax constant in log2 units per raw score unit (descales folded in for FP8).
+  float c = p.scale * LOG2E;
+  float vds = 1.f;
+  if (FP8) {
+    const float dq = p.qds[p.per_head ? h : 0];
+    const float dk = p.kds[p.per_head ? hkv : 0];
+    vds = p.vds[p.per_head ? hkv : 0];
+    c *= dq * dk;
+  }
+
+  // ---- Q^T fragments (B operand), held for the whole key loop -------------------
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
+  QFrag qf[QT][C::KS];
+  {
+    const size_t qstride = (size_t)p.Hq * DQK * C::EB;
+    const char* qbase = (const char*)p.q + ((size_t)b * N * p.Hq + h) * DQK * C::EB;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int qrow = q0w + 32 * t + l32;
+      const bool ok = qrow < N;
+      const char* rp = qbase + (size_t)(ok ? qrow : 0) * qstride;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (FP8) {
+          const uint4* src = (const uint4*)(rp + 64 * ks + 32 * g);
+          uint4 a = ok ? src[0] : make_uint4(0, 0, 0, 0);
+          uint4 bb = ok ? src[1] : make_uint4(0, 0, 0, 0);
+          i32x8 f;
+          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+          f[4] = bb.x; f[5] = bb.y; f[6] = bb.z; f[7] = bb.w;
+          qf[t][ks] = *(QFrag*)&f;
+        } else {
+          uint4 a = ok ? *(const uint4*)(rp + 2 * (16 * ks + 8 * g)) : make_uint4(0, 0, 0, 0);
+          qf[t][ks] = *(QFrag*)&a;
+        }
+      }
+    }
+  }
+
+  // ---- K/V tile staging: global -> registers -> LDS (double buffered) -----------
+  uint4 kreg[C::KPT];
+  typedef typename std::conditional<FP8, uint2, uint4>::type VLoad;
+  VLoad vreg[C::VPT][4];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int cix = 0; cix < C::KPT; ++cix) {
+      const int cc = tid + cix * C::NT;
+      if (cc < C::KCH) {
+        const int row = cc / C::R16, col = cc - row * C::R16;
+        const int key = kt * BN + row;
+        kreg[cix] = key < N ? *(const uint4*)(kbase + (size_t)key * kstride + col * 16)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::VPT; ++u) {
+      const int uu = tid + u * C::NT;
+      if (uu < C::VUN) {
+        const int dc = uu & 15, kg = uu >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kt * BN + 4 * kg + j;
+          const char* src = vbase + (size_t)key * vstride + dc * 8 * C::EB;
+          if (key < N) {
+            vreg[u][j] = *(const VLoad*)src;
+          } else {
+            vreg[u][j] = VLoad{};
+          }
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    char* ks_ = lds + buf * C::STAGE;
+    char* vs_ = ks_ + C::K_BYTES;
+#pragma unroll
+    for (int cix = 0; cix < C::KPT; ++cix) {
+      const int cc = tid + cix * C::NT;
+      if (cc < C::KCH) {
+        const int row = cc / C::R16, col = cc - row * C::R16;
+        *(uint4*)(ks_ + row * C::KROW + col * 16) = kreg[cix];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::VPT; ++u) {
+      const int uu = tid + u * C::NT;
+      if (uu < C::VUN) {
+        const int dc = uu & 15, kg = uu >> 4;
+        const int pos = vpos_of_group<FP8>(kg);
+        if (FP8) {
+          // 4 keys x 8 channels of bytes -> 8 rows (channels) of 4 key bytes.
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t a0 = w ? vreg[u][0].y : vreg[u][0].x;
+            const uint32_t a1 = w ? vreg[u][1].y : vreg[u][1].x;
+            const uint32_t a2 = w ? vreg[u][2].y : vreg[u][2].x;
+            const uint32_t a3 = w ? vreg[u][3].y : vreg[u][3].x;
+            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+            const uint32_t o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+            const uint32_t o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+            const uint32_t o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+            const uint32_t o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+            const int d0 = dc * 8 + 4 * w;
+            *(uint32_t*)(vs_ + (d0 + 0) * C::VROW + pos) = o0;
+            *(uint32_t*)(vs_ + (d0 + 1) * C::VROW + pos) = o1;
+            *(uint32_t*)(vs_ + (d0 + 2) * C::VROW + pos) = o2;
+            *(uint32_t*)(vs_ + (d0 + 3) * C::VROW + pos) = o3;
+          }
+        } else {
+          // 4 keys x 8 channels of bf16 -> 8 rows (channels) of 4 keys (8 bytes).
+          const uint32_t* r0 = (const uint32_t*)&vreg[u][0];
+          const uint32_t* r1 = (const uint32_t*)&vreg[u][1];
+          const uint32_t* r2 = (const uint32_t*)&vreg[u][2];
+          const uint32_t* r3 = (const uint32_t*)&vreg[u][3];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
+              uint2 val;
+              val.x = __builtin_amdgcn_perm(r1[w], r0[w], sel);
+              val.y = __builtin_amdgcn_perm(r3[w], r2[w], sel);
+              const int d = dc * 8 + 2 * w + hh;
+              *(uint2*)(vs_ + d * C::VROW + 2 * pos) = val;
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // ---- per-query running state ---------------------------------------------------
+  f32x16 oacc[QT][DV / 32];
+  float m_run[QT], l_run[QT], lx_run[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+    lx_run[t] = 0.f;
+#pragma unroll
+    for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[t][md][i] = 0.f;
+  }
+
+  const int wg_end = min(q0 + C::BM, N);
+  const int n_kt = (wg_end + BN - 1) / BN;                 // tiles the workgroup loads
+  const int w_end = min(q0w + QT * 32, N);
+  const int w_kt = q0w < N ? (w_end + BN - 1) / BN : 0;    // tiles this wave needs
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+
+    if (kt < w_kt) {
+      const char* ks_ = lds + buf * C::STAGE;
+      const char* vs_ = ks_ + C::K_BYTES;
+
+      // S^T = K Q^T : two 32-key M-tiles x QT query N-tiles
+      f32x16 s[2][QT];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[m][t][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const char* rp = ks_ + (32 * m + l32) * C::KROW;
+          if (FP8) {
+            const uint4 a = *(const uint4*)(rp + 64 * ks + 32 * g);
+            const uint4 bb = *(const uint4*)(rp + 64 * ks + 32 * g + 16);
+            i32x8 kf;
+            kf[0] = a.x; kf[1] = a.y; kf[2] = a.z; kf[3] = a.w;
+            kf[4] = bb.x; kf[5] = bb.y; kf[6] = bb.z; kf[7] = bb.w;
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+              s[m][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  kf, *(i32x8*)&qf[t][ks], s[m][t], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+          } else {
+            const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
+            const bf16x8 kf = *(const bf16x8*)&a;
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+              s[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, *(bf16x8*)&qf[t][ks],
+                                                                s[m][t], 0, 0, 0);
+          }
+        }
+      }
+
+      // causal mask on the tile(s) that cross this wave's diagonal
+      const bool diag = kt * BN + BN - 1 > q0w;
+      if (diag) {
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          const int qrow = q0w + 32 * t + l32;
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kt * BN + 32 * m + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key > qrow) s[m][t][i] = -INFINITY;
+            }
+        }
+      }
+
+      if (FP8) {
+        i32x8 pf[QT];
+        int psc[QT];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[m][t][i]);
+          mx = fmaxf(mx, xor32(mx));
+          const float m_new = fmaxf(m_run[t], mx);
+          const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
+          m_run[t] = m_new;
+          // block exponent: block max 2^(x_max + k) in (2^7, 2^8]
+          const float xmax = (mx - m_new) * c;
+          const float kbf = fminf(floorf(8.f - xmax), 127.f);
+          const int kb = (int)kbf;
+          psc[t] = 127 - kb;
+          const float A = 8.f * c;
+          const float Bc = fmaf(-A, m_new, 8.f * kbf + LEANP_C0);
+          uint32_t w[8];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const float val = fmaf(s[e >> 4][t][e & 15], A, Bc);
+            const uint32_t old = (e & 3) ? w[e >> 2] : 0u;
+            w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(val, e & 3, old);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[t][e] = (int)w[e];
+          if (WANT_LSE) {
+            const float nmc = -m_new * c;
+            float lx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+              lx += __builtin_amdgcn_exp2f(fmaf(s[e >> 4][t][e & 15], c, nmc));
+            lx_run[t] = lx_run[t] * alpha + lx;
+          }
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[t][md][i] *= alpha;
+        }
+        // O^T += V^T P^T, block scale removed by the scaled MFMA
+#pragma unroll
+        for (int md = 0; md < DV / 32; ++md) {
+          const char* rp = vs_ + (32 * md + l32) * C::VROW + 32 * g;
+          const uint4 a = *(const uint4*)(rp);
+          const uint4 bb = *(const uint4*)(rp + 16);
+          i32x8 vf;
+          vf[0] = a.x; vf[1] = a.y; vf[2] = a.z; vf[3] = a.w;
+          vf[4] = bb.x; vf[5] = bb.y; vf[6] = bb.z; vf[7] = bb.w;
+#pragma unroll
+          for (int t = 0; t < QT; ++t)
+            oacc[t][md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                vf, pf[t], oacc[t][md], 0, 0, 0, 0x7f7f7f7f, 0, psc[t]);
+        }
+        // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
+        i32x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          f32x16 z;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[i] = 0.f;
+          z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[t], z, 0, 0, 0,
+                                                              0x7f7f7f7f, 0, psc[t]);
+          l_run[t] += z[0];
+        }
+      } else {
+        bf16x8 pf[QT][4];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[m][t][i]);
+          mx = fmaxf(mx, xor32(mx));
+          const float m_new = fmaxf(m_run[t], mx);
+          const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
+          m_run[t] = m_new;
+          const float nmc = -m_new * c;
+          float rs = 0.f;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][t][e & 15], c, nmc));
+            rs += pv;
+            pf[t][e >> 3][e & 7] = (__bf16)pv;
+          }
+          l_run[t] = l_run[t] * alpha + rs;
+#pragma unroll
+          for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[t][md][i] *= alpha;
+        }
+        // O^T += V^T P^T over 4 k-steps of 16 keys
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+          for (int md = 0; md < DV / 32; ++md) {
+            const uint4 a =
+                *(const uint4*)(vs_ + (32 * md + l32) * C::VROW + 2 * (16 * kk + 8 * g));
+            const bf16x8 vf = *(const bf16x8*)&a;
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+              oacc[t][md] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][kk], oacc[t][md], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int qrow = q0w + 32 * t + l32;
+    float l = l_run[t];
+    if (!FP8) l += xor32(l);
+    float lsum = l;
+    if (FP8 && WANT_LSE) lsum = lx_run[t] + xor32(lx_run[t]);
+    const float inv = (FP8 ? vds : 1.f) / l;
+    if (qrow < N) {
+      __bf16* orow = (__bf16*)p.o + ((size_t)(b * N + qrow) * p.Hq + h) * DV;
+#pragma unroll
+      for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[t][md][4 * r + e] * inv);
+          *(bf16x4*)(orow + 32 * md + 8 * r + 4 * g) = ov;
+        }
+      if (WANT_LSE && g == 0)
+        p.lse[((size_t)b * p.Hq + h) * N + qrow] =
+            (m_run[t] * c + __builtin_amdgcn_logf(lsum)) * LN2;
+    }
+  }
+}
+
+template <bool FP8, int DQK, int NW, int QT>
+static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
+  using C = Cfg<FP8, DQK, NW, QT>;
+  FwdParams p = p0;
+  p.n_qtiles = (p.N + C::BM - 1) / C::BM;
+  const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (p.lse) {
+    auto kern = attn_fwd_kernel<FP8, DQK, NW, QT, true>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
+  } else {
+    auto kern = attn_fwd_kernel<FP8, DQK, NW, QT, false>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream) {
+  if (fp8) {
+    if (d_qk == 128) return launch_cfg<true, 128, 4, 2>(p, stream);
+    return launch_cfg<true, 192, 4, 2>(p, stream);
+  }
+  if (d_qk == 128) return launch_cfg<false, 128, 4, 2>(p, stream);
+  return launch_cfg<false, 192, 4, 2>(p, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,120 @@
+/*
+ * attn.h -- C ABI of libattn: causal forward (prefill) attention for AMD
+ * Instinct MI355X (CDNA4, gfx950), in BF16 and FP8 e4m3, for head dim 128
+ * with grouped KV heads and for the MLA shape (d_qk = 192, d_v = 128).
+ *
+ * What is computed (the-ai.news "Waarom presteert FP8 minder goed op de
+ * MI355X?"; spke.com "TL;DR"; ai-daily-news.org "Qué cubren los kernels"):
+ * for every batch b, query head h and query i,
+ *     O[b,i,h,:]  = sum_{j<=i} softmax_j(scale * Q[b,i,h,:].K[b,j,g,:]) V[b,j,g,:]
+ *     LSE[b,h,i]  = log sum_{j<=i} exp(scale * Q[b,i,h,:].K[b,j,g,:])
+ * with g = h / (Hq / Hkv) (consecutive query heads share a KV head), computed
+ * tile by tile with an online softmax so the N x N score matrix is never
+ * stored (kongchang.com "为什么 prefill attention 值得单独优化").
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory, keeps no state between calls and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL means the null stream) and the call returns at once.
+ *   - Layouts are contiguous "BSHD", head dim innermost:
+ *       q (B, N, Hq,  d_qk)   k (B, N, Hkv, d_qk)   v (B, N, Hkv, d_v)
+ *       o (B, N, Hq,  d_v)  bf16        lse (B, Hq, N) float32
+ *     q, k, v, o must be 16-byte aligned; lse and descale pointers 4-byte
+ *     aligned.
+ *   - Accepted shapes: B >= 1, N >= 1, Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
+ *     (d_qk, d_v) in {(128, 128), (192, 128)}, softmax_scale finite and > 0,
+ *     and every tensor smaller than 2^31 elements.  Anything else is rejected
+ *     before any launch.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_E_* code; no call aborts
+ *     and no exception crosses the ABI.  attn_status_string() names a code.
+ *   - NaN or Inf inputs give undefined output values but no fault.
+ *   - Calls are thread-safe.  Results are bit-identical across repeated runs
+ *     on the same device (no atomics or split reductions in the attention
+ *     kernels; spke.com "ZYFAのFP8アテンションの精度はどのくらいか?" reports
+ *     bit-identical outputs across repeated runs).
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_INVAL = -1,        /* bad size, scale, NULL pointer or flag           */
+  ATTN_E_UNSUPPORTED = -2,  /* (d_qk, d_v) not one of the supported pairs      */
+  ATTN_E_ALIGN = -3,        /* a tensor pointer is not 16-byte aligned         */
+  ATTN_E_NODEVICE = -4,     /* no usable HIP device                            */
+  ATTN_E_LAUNCH = -5        /* the HIP runtime reported a launch error (this
+                               includes a device without gfx950 code)          */
+};
+
+/*
+ * BF16 causal attention.
+ *   q, k, v   bf16 inputs in the layouts above.
+ *   o         bf16 output (B, N, Hq, d_v), written in full.
+ *   lse       float32 (B, Hq, N) natural-log log-sum-exp of the scaled scores,
+ *             or NULL to skip it.
+ *   softmax_scale  multiplies Q.K before the softmax (usually 1/sqrt(d_qk)).
+ * Scores and the O accumulator are float32; probabilities enter the P.V
+ * product as bf16.
+ */
+int attn_fwd_causal_bf16(const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                         float softmax_scale, void* stream);
+
+/*
+ * FP8 causal attention (spke.com "ZYFAはどのように動作するのか?"; the-ai.news
+ * "Drie technieken om de bottleneck te omzeilen").
+ *   q, k, v   OCP e4m3fn codes (uint8) in the layouts above; the value of a
+ *             code c of head h is e4m3(c) * descale.
+ *   q_descale, k_descale, v_descale  DEVICE float32 pointers: one value each
+ *             when descale_per_head == 0, else Hq (q) / Hkv (k, v) values.
+ *   o, lse    as for the BF16 entry point (o is bf16).
+ * Q.K^T and P.V run on the e4m3 matrix instructions with float32
+ * accumulation.  Each probability is written straight as an e4m3 code from
+ * one multiply-add and one integer conversion, using that the code of 2^x is
+ * about 8x plus a constant; each 64-key block of probabilities is scaled by a
+ * power of two that the scaled matrix instruction removes, and O is divided
+ * by the sum of the rounded probabilities.  When lse != NULL the log-sum-exp
+ * comes from a separate float32 sum of exact exponentials (the rounded sum is
+ * too coarse for it); lse == NULL skips that work.
+ */
+int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                        const float* q_descale, const float* k_descale,
+                        const float* v_descale, int descale_per_head,
+                        void* o, float* lse,
+                        int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                        float softmax_scale, void* stream);
+
+/*
+ * Absmax quantisation of a float32 (B, N, H, d) tensor into e4m3fn codes
+ * (kongchang.com "ZYFA 的性能与精度数据": per-tensor or per-head scale
+ * factors map values into the e4m3 range).
+ *   x         DEVICE float32 input, contiguous (B, N, H, d), 16-byte aligned.
+ *   out       DEVICE uint8 output of the same shape, 4-byte aligned.
+ *   descale   DEVICE float32 output: 1 value (per_head == 0) or H values.
+ *             descale = absmax / 448 in float32 (1 for an all-zero tensor or
+ *             head); it is also used as scratch during the call.
+ *   code      = round-to-nearest-even e4m3 of the float32 quotient x / descale,
+ *             saturating at +-448; NaN maps to 0x7F.
+ * d must be a multiple of 4, H <= 65535 and the tensor below 2^31 elements.
+ * Invalid arguments return ATTN_E_INVAL / ATTN_E_ALIGN before any launch.  The absmax reduction is order-independent, so
+ * results are bit-identical across runs.  Four kernels are enqueued.
+ */
+int quantize_e4m3(const float* x, uint8_t* out, float* descale,
+                  int B, int N, int H, int d, int per_head, void* stream);
+
+/* Static, NUL-terminated name of a status code; never NULL. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

@@ -22,9 +22,10 @@ rows of P summing to one, GQA == repeated-KV MHA) and brute-force loops on tiny
 inputs.  No function here is "parity unpinned".
 """
 from .formats import (bf16_decode, e4m3_decode, e4m3_encode, quantize_e4m3,
-                      E4M3_MAX)
+                      absmax_descale, encode_with_descale, E4M3_MAX)
 from .attention import (causal_attention, causal_attention_rows, kv_head_of,
                         visible_keys)
 
-__all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "E4M3_MAX",
+__all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "absmax_descale",
+           "encode_with_descale", "E4M3_MAX",
            "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys"]

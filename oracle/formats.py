@@ -82,6 +82,27 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def absmax_descale(x: np.ndarray, per_head: bool) -> np.ndarray:
+    """descale of a (B, N, H, d) float32 tensor: float32(absmax) / float32(448)
+    per head ((H,)) or per tensor ((1,)); 1 where the absmax is 0."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 4:
+        raise ValueError("expected (B, N, H, d)")
+    if per_head:
+        amax = np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
+    else:
+        amax = np.array([np.max(np.abs(x))], dtype=np.float32)
+    descale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return np.where(amax > 0, descale, np.float32(1.0)).astype(np.float32)
+
+
+def encode_with_descale(x: np.ndarray, descale) -> np.ndarray:
+    """e4m3 codes of the float32 quotient x / descale (descale broadcast
+    against x; float32 / float32 is correctly rounded)."""
+    qv = (np.asarray(x, dtype=np.float32) / np.asarray(descale, dtype=np.float32)).astype(np.float32)
+    return e4m3_encode(qv)
+
+
 def quantize_e4m3(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, np.ndarray]:
     """Absmax quantisation of a (B, N, H, d) float32 tensor.
 
@@ -91,15 +112,6 @@ def quantize_e4m3(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, np.ndarray
     the float32 quotient x / descale, so code * descale reproduces x to within
     e4m3's half-spacing.
     """
-    x = np.asarray(x, dtype=np.float32)
-    if x.ndim != 4:
-        raise ValueError("expected (B, N, H, d)")
-    if per_head:
-        amax = np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
-    else:
-        amax = np.array([np.max(np.abs(x))], dtype=np.float32)
-    descale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    descale = np.where(amax > 0, descale, np.float32(1.0)).astype(np.float32)
+    descale = absmax_descale(x, per_head)
     ds = descale[None, None, :, None] if per_head else descale[0]
-    qv = (x / ds).astype(np.float32)   # float32 / float32: correctly rounded
-    return e4m3_encode(qv), descale
+    return encode_with_descale(x, ds), descale

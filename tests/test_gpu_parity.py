@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and mid sizes compare every output element; the full 16K/32K workloads
+compare sampled rows (the oracle computes them one by one) in the same launch
+configuration the benchmark times.  Also: quantize_e4m3 bit-exact against the
+oracle's encoder, run-to-run byte identity, causality under perturbation of
+later keys, GQA == MHA with repeated K/V, and the equal-scores closed form.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import (bf16_bytes, check, gpu_quantize, note, run_bf16, run_fp8)
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.CONFIGS
+
+
+def _small_cases():
+    g = W["tiny"]
+    return {
+        "tiny": W["tiny"],
+        "mid_gqa": W["mid_gqa"],
+        "ragged_gqa_n300_b2": g.with_(name="ragged", B=2, Hq=8, Hkv=2, N=300, seed=21),
+        "n1": g.with_(name="n1", N=1, seed=22),
+        "n33": g.with_(name="n33", Hq=4, Hkv=1, N=33, seed=23),
+        "n65_b3": g.with_(name="n65", B=3, N=65, seed=24),
+        "mistral_n1024": W["mistral16k"].with_(N=1024, seed=25),
+        "mla_n700": W["mla16k"].with_(N=700, Hq=4, Hkv=4, seed=26),
+        "mla_n256_per_tensor": W["mla16k"].with_(N=256, Hq=2, Hkv=2, fp8_per_head=False, seed=27),
+    }
+
+
+SMALL = _small_cases()
+
+
+def _oracle_bf16(x, w):
+    qu, ku, vu = (bf16_bytes(x[n]) for n in "qkv")
+    dec = [oracle.bf16_decode(a) for a in (qu, ku, vu)]
+    return (qu, ku, vu), dec
+
+
+def _fp8_inputs(x, w):
+    """GPU-quantised device codes + oracle-quantised host codes; asserts equality."""
+    dev, host = [], []
+    for n in "qkv":
+        codes_d, ds_d = gpu_quantize(x[n], w.fp8_per_head)
+        codes_h, ds_h = oracle.quantize_e4m3(x[n], w.fp8_per_head)
+        cd = codes_d.cpu().numpy()
+        assert np.array_equal(cd, codes_h), f"quantize_e4m3({n}) codes differ from the oracle"
+        assert np.array_equal(ds_d.cpu().numpy().view(np.uint32), ds_h.view(np.uint32)), n
+        dev.append((codes_d, ds_d))
+        host.append(oracle.e4m3_decode(codes_h) * (ds_h[None, None, :, None].astype(np.float64)
+                                                   if w.fp8_per_head else float(ds_h[0])))
+    return dev, host
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_bf16_parity_full(case):
+    w = SMALL[case]
+    note(f"case bf16 {case}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d_qk}/{w.d_v}")
+    x = workloads.generate(w)
+    (qu, ku, vu), (q, k, v) = _oracle_bf16(x, w)
+    out = run_bf16(qu, ku, vu, w.softmax_scale)[0]
+    ro, rl = oracle.causal_attention(q, k, v, w.softmax_scale)
+    check(case, "bf16", out.o, ro, out.lse, rl)
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_fp8_parity_full(case):
+    w = SMALL[case]
+    note(f"case fp8 {case}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d_qk}/{w.d_v} "
+         f"per_head={w.fp8_per_head}")
+    x = workloads.generate(w)
+    dev, (q, k, v) = _fp8_inputs(x, w)
+    (qc, qd), (kc, kd), (vc, vd) = dev
+    out = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale)[0]
+    ro, rl = oracle.causal_attention(q, k, v, w.softmax_scale)
+    check(case, "fp8", out.o, ro, out.lse, rl)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_without_lse_same_output(prec):
+    """lse=NULL skips the LSE work but leaves O unchanged (byte-identical)."""
+    w = SMALL["ragged_gqa_n300_b2"]
+    x = workloads.generate(w)
+    if prec == "bf16":
+        (qu, ku, vu), _ = _oracle_bf16(x, w)
+        a = run_bf16(qu, ku, vu, w.softmax_scale, want_lse=True)[0]
+        b = run_bf16(qu, ku, vu, w.softmax_scale, want_lse=False)[0]
+    else:
+        dev, _ = _fp8_inputs(x, w)
+        (qc, qd), (kc, kd), (vc, vd) = dev
+        a = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, want_lse=True)[0]
+        b = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, want_lse=False)[0]
+    assert a.o_bytes == b.o_bytes
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_deterministic_repeats(prec):
+    w = W["mid_gqa"]
+    x = workloads.generate(w)
+    if prec == "bf16":
+        (qu, ku, vu), _ = _oracle_bf16(x, w)
+        outs = run_bf16(qu, ku, vu, w.softmax_scale, repeats=20)
+    else:
+        dev, _ = _fp8_inputs(x, w)
+        (qc, qd), (kc, kd), (vc, vd) = dev
+        outs = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, repeats=20)
+    for o in outs[1:]:
+        assert o.o_bytes == outs[0].o_bytes and o.lse_bytes == outs[0].lse_bytes
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_causality_under_perturbation(prec):
+    """Rewriting K/V rows >= c leaves O and LSE rows < c byte-identical."""
+    w = W["tiny"].with_(B=1, Hq=4, Hkv=2, N=520, seed=31)
+    x = workloads.generate(w)
+    rng = np.random.default_rng(99)
+    for c in (1, 64, 257, 519):
+        y = {n: a.copy() for n, a in x.items()}
+        y["k"][:, c:] = rng.standard_normal(y["k"][:, c:].shape).astype(np.float32) * 0.5
+        y["v"][:, c:] = rng.standard_normal(y["v"][:, c:].shape).astype(np.float32) * 0.5
+        if prec == "bf16":
+            (qu, ku, vu), _ = _oracle_bf16(x, w)
+            (qu2, ku2, vu2), _ = _oracle_bf16(y, w)
+            a = run_bf16(qu, ku, vu, w.softmax_scale)[0]
+            b = run_bf16(qu2, ku2, vu2, w.softmax_scale)[0]
+        else:
+            # quantise the unperturbed draw, then rewrite later codes only, so the
+            # descales (and so every earlier input value) stay the same
+            dev, _ = _fp8_inputs(x, w)
+            (qc, qd), (kc, kd), (vc, vd) = dev
+            kc2, vc2 = kc.clone(), vc.clone()
+            for t in (kc2, vc2):   # random finite codes (never 0x7F / 0xFF)
+                r = rng.integers(0, 0x7F, size=t[:, c:].shape) | (rng.integers(0, 2, size=t[:, c:].shape) << 7)
+                t[:, c:] = torch.from_numpy(r.astype(np.uint8)).to(t.device)
+            a = run_fp8(qc, kc, vc, qd, kd, vd, False, w.softmax_scale)[0]
+            b = run_fp8(qc, kc2, vc2, qd, kd, vd, False, w.softmax_scale)[0]
+        assert np.array_equal(a.o[:, :c], b.o[:, :c]), c
+        assert np.array_equal(a.lse[:, :, :c], b.lse[:, :, :c]), c
+        assert not np.array_equal(a.o[:, c:], b.o[:, c:]), c
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_gqa_equals_repeated_mha(prec):
+    w = W["tiny"].with_(B=2, Hq=8, Hkv=2, N=200, seed=32)
+    x = workloads.generate(w)
+    G = w.Hq // w.Hkv
+    xr = {"q": x["q"], "k": np.ascontiguousarray(np.repeat(x["k"], G, axis=2)),
+          "v": np.ascontiguousarray(np.repeat(x["v"], G, axis=2))}
+    if prec == "bf16":
+        a = run_bf16(*_oracle_bf16(x, w)[0], w.softmax_scale)[0]
+        b = run_bf16(*_oracle_bf16(xr, w)[0], w.softmax_scale)[0]
+    else:
+        wr = w.with_(Hkv=w.Hq)
+        (qc, qd), (kc, kd), (vc, vd) = _fp8_inputs(x, w.with_(fp8_per_head=False))[0]
+        a = run_fp8(qc, kc, vc, qd, kd, vd, False, w.softmax_scale)[0]
+        (qc, qd), (kc, kd), (vc, vd) = _fp8_inputs(xr, wr.with_(fp8_per_head=False))[0]
+        b = run_fp8(qc, kc, vc, qd, kd, vd, False, w.softmax_scale)[0]
+    assert a.o_bytes == b.o_bytes and a.lse_bytes == b.lse_bytes
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_equal_scores_mean_of_v(prec):
+    """Q = 0: O_i = mean(V_0..V_i) and LSE_i = ln(i+1)."""
+    w = W["tiny"].with_(B=1, Hq=2, Hkv=1, N=300, seed=33)
+    x = workloads.generate(w)
+    x["q"][:] = 0.0
+    if prec == "bf16":
+        (qu, ku, vu), (_, _, v) = _oracle_bf16(x, w)
+        out = run_bf16(qu, ku, vu, w.softmax_scale)[0]
+    else:
+        dev, (_, _, v) = _fp8_inputs(x, w)
+        (qc, qd), (kc, kd), (vc, vd) = dev
+        out = run_fp8(qc, kc, vc, qd, kd, vd, False, w.softmax_scale)[0]
+    mean = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, w.N + 1)[:, None]
+    for h in range(w.Hq):
+        err = np.max(np.abs(out.o[0, :, h] - mean))
+        assert err < 2e-2, err
+        assert np.max(np.abs(out.lse[0, h] - np.log(np.arange(1, w.N + 1)))) < 1e-4
+
+
+# ---- full-size workloads, sampled rows -------------------------------------------
+
+FULL = ["mistral16k", "gauss32k", "mla16k", "mla32k"]
+
+
+def _sample_rows(w, n_rand=48, seed=7):
+    rng = np.random.default_rng(seed)
+    N = w.N
+    fixed_i = [0, 1, 63, 64, 255, 256, N // 2, N - 257, N - 256, N - 65, N - 1]
+    rows = []
+    for b in range(w.B):
+        for h in sorted({0, w.Hq - 1, w.Hq // 2}):
+            rows += [(b, h, i) for i in fixed_i]
+    rows += [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(N)))
+             for _ in range(n_rand)]
+    return rows
+
+
+@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_full_size_sampled_rows(name, prec):
+    w = W[name]
+    note(f"case full {prec} {name}: N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk}/{w.d_v}")
+    x = workloads.generate(w)
+    rows = _sample_rows(w)
+    bb = np.array([r[0] for r in rows])
+    hh = np.array([r[1] for r in rows])
+    ii = np.array([r[2] for r in rows])
+    if prec == "bf16":
+        (qu, ku, vu), (q, k, v) = _oracle_bf16(x, w)
+        outs = run_bf16(qu, ku, vu, w.softmax_scale, repeats=2)
+    else:
+        dev, (q, k, v) = _fp8_inputs(x, w)
+        (qc, qd), (kc, kd), (vc, vd) = dev
+        outs = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, repeats=2)
+    assert outs[0].o_bytes == outs[1].o_bytes and outs[0].lse_bytes == outs[1].lse_bytes
+    ro, rl = oracle.causal_attention_rows(q, k, v, w.softmax_scale, rows)
+    out = outs[0]
+    go = out.o[bb, ii, hh]
+    gl = out.lse[bb, hh, ii]
+    assert np.all(np.isfinite(out.o)) and np.all(np.isfinite(out.lse))
+    check(f"{name}/rows", prec, go, ro, gl, rl)

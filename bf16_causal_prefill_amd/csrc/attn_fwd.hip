@@ -6,29 +6,44 @@
 // softmax so the score matrix never leaves registers (kongchang.com,
 // "为什么 prefill attention 值得单独优化").
 //
-// Formulation.  Each wave owns QT x 32 queries.  For a tile of 64 keys it forms the
-// TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs (A = K rows from LDS, B = Q^T held in
-// registers for the whole loop), so that in the 32x32 accumulator a lane holds one
-// query column and 16 keys of it: the row max, the exponentials and the row sums are
-// per-lane work plus one exchange with the lane 32 apart.  The second product is also
-// transposed, O^T = V^T P^T: the B operand P^T needs, per lane, probabilities of its
-// own query, which are exactly the values the lane already holds, so P goes from the
-// score accumulator to the MFMA operand without any cross-lane movement.  The keys a
-// lane holds are not contiguous (rows 8*(i/4) + 4*(lane/32) + i%4 of the accumulator),
-// so V is written to LDS transposed (V^T, one row per head-dim channel) with the keys
-// of each row permuted so that the 8 (bf16) or 32 (fp8) keys a lane needs for one MFMA
-// are contiguous: the contraction over keys does not care about key order as long as
-// both operands use the same one.
+// Work split.  A workgroup owns NW*32 consecutive queries of one (batch, head); each of
+// its NW waves owns 32 of them.  The workgroup walks the key axis in tiles of BN keys
+// up to its causal diagonal; each K/V tile is copied HBM -> registers -> LDS once per
+// workgroup (double buffered: the loads of tile j+1 are in flight while tile j is
+// used) and every wave reads its matrix operands from LDS.  The launch asks for two
+// waves per SIMD, so while one wave waits on its matrix instructions the other issues
+// its softmax arithmetic.
+//
+// Formulation.  Each wave forms the TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs
+// (A = K rows from LDS, B = Q^T held in registers for the whole loop), so that in the
+// 32x32 accumulator a lane holds one query column and 16 keys of it: the row max, the
+// exponentials and the row sums are per-lane work.  The second product is also
+// transposed, O^T = V^T P^T: the B operand P^T needs, per lane, probabilities of its own
+// query, which are exactly the values the lane already holds, so P goes from the score
+// accumulator to the MFMA operand without any cross-lane movement.  The keys a lane
+// holds are not contiguous (rows 8*(i/4) + 4*(lane/32) + i%4 of the accumulator), so V
+// is written to LDS transposed (V^T, one row per head-dim channel) with the keys of each
+// row permuted so that the 8 (bf16) or 32 (fp8) keys a lane needs for one MFMA are
+// contiguous: the contraction over keys does not care about key order as long as both
+// operands use the same one.
+//
+// Lazy rescaling.  The running max m of a query only moves when a tile's max exceeds it
+// by more than TAU (log2 units); otherwise the tile's probabilities are taken relative to
+// the stale m (so they are at most 2^TAU, harmless in fp32 accumulators, in bf16, and
+// for FP8 absorbed by the block exponent below).  The rescale of O by 2^(m_old - m_new)
+// then runs on only a handful of tiles per row instead of on every tile.
 //
 // FP8 probabilities (the-ai.news "Drie technieken om de bottleneck te omzeilen";
 // spke.com "Lean P" and "ブロックごとのスケーリングと丸められた行和"): the e4m3 code of
 // 2^y is 8y + 56 exactly at integer y and in between linear in y, so a probability
 // 2^(x + k) is written as the integer conversion of one FMA, s * 8c + (8k + C0 - 8c m).
-// k is a per-query, per-64-key-block power of two chosen so that the block maximum lands
-// in (2^7, 2^8] (codes <= 0x78) and small probabilities stay in the normal range; the
-// scaled MFMA's E8M0 operand scale 2^-k undoes it at no cost.  O is divided by the sum of
-// the same rounded probabilities, taken with one extra MFMA per block against a matrix
-// of ones, so the approximation's bias cancels in the normalisation.
+// k is a power-of-two block exponent chosen per query and 64-key block, so that the
+// block maximum lands in (2^7, 2^8] (codes <= 0x78) and small probabilities stay in
+// the normal range; the scaled MFMA's E8M0 operand scale 2^-k (the same value for
+// both of its 32-key scale blocks) undoes it at no cost.  O is
+// divided by the sum of the same rounded probabilities, taken with one extra MFMA per
+// 64-key block against a matrix of ones, so the approximation's bias cancels in the
+// normalisation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,10 +55,10 @@ namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BN = 64;     // keys per tile; also the FP8 probability scaling block
 constexpr int DV = 128;    // value head dim (both supported shapes)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -51,12 +66,15 @@ constexpr float LN2 = 0.6931471805599453f;
 // conversion, which rounds to nearest; 56 - 0.5 makes it act as truncation of
 // 8*log2(p) + 56, which keeps the piecewise-linear code close to unbiased.
 constexpr float LEANP_C0 = 55.5f;
+// Lazy-rescale threshold in log2 units (probabilities relative to a stale max stay
+// below 2^TAU).
+constexpr float TAU = 8.0f;
 
-template <bool FP8, int DQK, int NW, int QT>
+template <bool FP8, int DQK, int BN, int NW>
 struct Cfg {
   static constexpr int EB = FP8 ? 1 : 2;            // bytes per element
   static constexpr int NT = NW * 64;                 // threads per workgroup
-  static constexpr int BM = NW * QT * 32;            // queries per workgroup
+  static constexpr int BM = NW * 32;                 // queries per workgroup
   static constexpr int KRB = DQK * EB;               // K row bytes
   static constexpr int KROW = KRB + 16;              // padded LDS row (bank spread)
   static constexpr int R16 = KRB / 16;               // 16-byte chunks per K row
@@ -70,14 +88,18 @@ struct Cfg {
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int LDS = 2 * STAGE;              // double buffered
   static constexpr int KS = FP8 ? DQK / 64 : DQK / 16;  // MFMA k-steps of Q K^T
+  static constexpr int MT = BN / 32;                 // 32-key M-tiles of S^T
+  static constexpr int NB = BN / 64;                 // 64-key blocks
+  static_assert(BN % 64 == 0, "key tile must be a multiple of 64");
 };
 
-// Position of key `k` (0..63) inside a V^T row of the LDS tile: the keys one lane
-// feeds to one P V MFMA become contiguous (see the file comment).
+// Position of key `key` (0..BN-1) inside a V^T row of the LDS tile: the keys one lane
+// feeds to one P V MFMA become contiguous (see the file comment).  Works on groups of
+// 4 keys (kg = key / 4), which stay contiguous.
 template <bool FP8>
-__device__ __forceinline__ int vpos_of_group(int kg) {   // kg = key / 4
-  if (FP8) {  // key = 32m + 8a + 4g + b  ->  32g + 16m + 4a + b
-    return 32 * (kg & 1) + 16 * (kg >> 3) + 4 * ((kg >> 1) & 3);
+__device__ __forceinline__ int vpos_of_group(int kg) {
+  if (FP8) {  // key = 64n + 32m + 8a + 4g + b  ->  64n + 32g + 16m + 4a + b
+    return 64 * (kg >> 4) + 32 * (kg & 1) + 16 * ((kg >> 3) & 1) + 4 * ((kg >> 1) & 3);
   } else {    // key = 16s + 8a + 4g + b  ->  16s + 8g + 4a + b
     return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
   }
@@ -111,9 +133,27 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, i
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
-template <bool FP8, int DQK, int NW, int QT, bool WANT_LSE>
-__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
-  using C = Cfg<FP8, DQK, NW, QT>;
+// max(x[lane], x[lane ^ 32]) in every lane: one lane-half swap and one max.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ i32x8 load_i32x8(const char* p) {
+  const uint4 a = *(const uint4*)p;
+  const uint4 b = *(const uint4*)(p + 16);
+  i32x8 f;
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  return f;
+}
+
+template <bool FP8, int DQK, int BN, int NW, bool WANT_LSE>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdParams p) {
+  using C = Cfg<FP8, DQK, BN, NW>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -127,7 +167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
   const int hkv = h / (p.Hq / p.Hkv);
   const int N = p.N;
   const int q0 = qt * C::BM;
-  const int q0w = q0 + wave * QT * 32;
+  const int q0w = q0 + wave * 32;
 
   const size_t kstride = (size_t)p.Hkv * DQK * C::EB;   // bytes between keys
   const size_t vstride = (size_t)p.Hkv * DV * C::EB;
@@ -145,64 +185,74 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- Q^T fragments (B operand), held for the whole key loop -------------------
+  // Rows past N read row N-1 (finite data); their outputs are never stored.
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
-  QFrag qf[QT][C::KS];
+  QFrag qf[C::KS];
   {
     const size_t qstride = (size_t)p.Hq * DQK * C::EB;
     const char* qbase = (const char*)p.q + ((size_t)b * N * p.Hq + h) * DQK * C::EB;
+    const int qrow = min(q0w + l32, N - 1);
+    const char* rp = qbase + (size_t)qrow * qstride;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int qrow = q0w + 32 * t + l32;
-      const bool ok = qrow < N;
-      const char* rp = qbase + (size_t)(ok ? qrow : 0) * qstride;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        if (FP8) {
-          const uint4* src = (const uint4*)(rp + 64 * ks + 32 * g);
-          uint4 a = ok ? src[0] : make_uint4(0, 0, 0, 0);
-          uint4 bb = ok ? src[1] : make_uint4(0, 0, 0, 0);
-          i32x8 f;
-          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-          f[4] = bb.x; f[5] = bb.y; f[6] = bb.z; f[7] = bb.w;
-          qf[t][ks] = *(QFrag*)&f;
-        } else {
-          uint4 a = ok ? *(const uint4*)(rp + 2 * (16 * ks + 8 * g)) : make_uint4(0, 0, 0, 0);
-          qf[t][ks] = *(QFrag*)&a;
-        }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if constexpr (FP8) {
+        qf[ks] = load_i32x8(rp + 64 * ks + 32 * g);
+      } else {
+        const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
+        qf[ks] = *(const QFrag*)&a;
       }
     }
   }
 
   // ---- K/V tile staging: global -> registers -> LDS (double buffered) -----------
+  // Buffer loads: each thread copies the same byte offsets of every tile, the tile's
+  // base address goes into the (uniform) buffer descriptor, and the descriptor's range
+  // ends at key N-1 of this sequence, so the keys past N in the last tile read as
+  // zeros (they are masked: key > every query row).
   uint4 kreg[C::KPT];
   typedef typename std::conditional<FP8, uint2, uint4>::type VLoad;
   VLoad vreg[C::VPT][4];
+  uint32_t koff[C::KPT], voff[C::VPT][4];
+#pragma unroll
+  for (int cix = 0; cix < C::KPT; ++cix) {
+    const int cc = tid + cix * C::NT;
+    const int row = cc / C::R16, col = cc - row * C::R16;
+    koff[cix] = (uint32_t)row * (uint32_t)kstride + (uint32_t)col * 16u;
+  }
+#pragma unroll
+  for (int u = 0; u < C::VPT; ++u) {
+    const int uu = tid + u * C::NT;
+    const int dc = uu & 15, kg = uu >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      voff[u][j] = (uint32_t)(4 * kg + j) * (uint32_t)vstride + (uint32_t)(dc * 8 * C::EB);
+  }
 
   auto load_tile = [&](int kt) {
+    const int keys_left = N - kt * BN;   // >= 1
+    const int kbytes = (keys_left - 1) * (int)kstride + C::KRB;
+    const int vbytes = (keys_left - 1) * (int)vstride + DV * C::EB;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)kt * BN * kstride), (short)0, kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (size_t)kt * BN * vstride), (short)0, vbytes, 0x00020000);
 #pragma unroll
     for (int cix = 0; cix < C::KPT; ++cix) {
-      const int cc = tid + cix * C::NT;
-      if (cc < C::KCH) {
-        const int row = cc / C::R16, col = cc - row * C::R16;
-        const int key = kt * BN + row;
-        kreg[cix] = key < N ? *(const uint4*)(kbase + (size_t)key * kstride + col * 16)
-                            : make_uint4(0, 0, 0, 0);
-      }
+      if (C::KCH % C::NT != 0 && tid + cix * C::NT >= C::KCH) break;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[cix], 0, 0);
+      kreg[cix] = *(const uint4*)&x;
     }
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
-      const int uu = tid + u * C::NT;
-      if (uu < C::VUN) {
-        const int dc = uu & 15, kg = uu >> 4;
+      if (C::VUN % C::NT != 0 && tid + u * C::NT >= C::VUN) break;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kt * BN + 4 * kg + j;
-          const char* src = vbase + (size_t)key * vstride + dc * 8 * C::EB;
-          if (key < N) {
-            vreg[u][j] = *(const VLoad*)src;
-          } else {
-            vreg[u][j] = VLoad{};
-          }
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, voff[u][j], 0, 0);
+          vreg[u][j] = *(const VLoad*)&x;
+        } else {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[u][j], 0, 0);
+          vreg[u][j] = *(const VLoad*)&x;
         }
       }
     }
@@ -214,56 +264,54 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int cix = 0; cix < C::KPT; ++cix) {
       const int cc = tid + cix * C::NT;
-      if (cc < C::KCH) {
-        const int row = cc / C::R16, col = cc - row * C::R16;
-        *(uint4*)(ks_ + row * C::KROW + col * 16) = kreg[cix];
-      }
+      if (C::KCH % C::NT != 0 && cc >= C::KCH) break;
+      const int row = cc / C::R16, col = cc - row * C::R16;
+      *(uint4*)(ks_ + row * C::KROW + col * 16) = kreg[cix];
     }
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
       const int uu = tid + u * C::NT;
-      if (uu < C::VUN) {
-        const int dc = uu & 15, kg = uu >> 4;
-        const int pos = vpos_of_group<FP8>(kg);
-        if (FP8) {
-          // 4 keys x 8 channels of bytes -> 8 rows (channels) of 4 key bytes.
+      if (C::VUN % C::NT != 0 && uu >= C::VUN) break;
+      const int dc = uu & 15, kg = uu >> 4;
+      const int pos = vpos_of_group<FP8>(kg);
+      if constexpr (FP8) {
+        // 4 keys x 8 channels of bytes -> 8 rows (channels) of 4 key bytes.
 #pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const uint32_t a0 = w ? vreg[u][0].y : vreg[u][0].x;
-            const uint32_t a1 = w ? vreg[u][1].y : vreg[u][1].x;
-            const uint32_t a2 = w ? vreg[u][2].y : vreg[u][2].x;
-            const uint32_t a3 = w ? vreg[u][3].y : vreg[u][3].x;
-            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-            const uint32_t o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-            const uint32_t o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-            const uint32_t o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-            const uint32_t o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-            const int d0 = dc * 8 + 4 * w;
-            *(uint32_t*)(vs_ + (d0 + 0) * C::VROW + pos) = o0;
-            *(uint32_t*)(vs_ + (d0 + 1) * C::VROW + pos) = o1;
-            *(uint32_t*)(vs_ + (d0 + 2) * C::VROW + pos) = o2;
-            *(uint32_t*)(vs_ + (d0 + 3) * C::VROW + pos) = o3;
-          }
-        } else {
-          // 4 keys x 8 channels of bf16 -> 8 rows (channels) of 4 keys (8 bytes).
-          const uint32_t* r0 = (const uint32_t*)&vreg[u][0];
-          const uint32_t* r1 = (const uint32_t*)&vreg[u][1];
-          const uint32_t* r2 = (const uint32_t*)&vreg[u][2];
-          const uint32_t* r3 = (const uint32_t*)&vreg[u][3];
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t a0 = w ? vreg[u][0].y : vreg[u][0].x;
+          const uint32_t a1 = w ? vreg[u][1].y : vreg[u][1].x;
+          const uint32_t a2 = w ? vreg[u][2].y : vreg[u][2].x;
+          const uint32_t a3 = w ? vreg[u][3].y : vreg[u][3].x;
+          const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+          const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+          const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+          const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+          const uint32_t o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+          const uint32_t o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+          const uint32_t o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+          const uint32_t o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+          const int d0 = dc * 8 + 4 * w;
+          *(uint32_t*)(vs_ + (d0 + 0) * C::VROW + pos) = o0;
+          *(uint32_t*)(vs_ + (d0 + 1) * C::VROW + pos) = o1;
+          *(uint32_t*)(vs_ + (d0 + 2) * C::VROW + pos) = o2;
+          *(uint32_t*)(vs_ + (d0 + 3) * C::VROW + pos) = o3;
+        }
+      } else {
+        // 4 keys x 8 channels of bf16 -> 8 rows (channels) of 4 keys (8 bytes).
+        const uint32_t* r0 = (const uint32_t*)&vreg[u][0];
+        const uint32_t* r1 = (const uint32_t*)&vreg[u][1];
+        const uint32_t* r2 = (const uint32_t*)&vreg[u][2];
+        const uint32_t* r3 = (const uint32_t*)&vreg[u][3];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
-              uint2 val;
-              val.x = __builtin_amdgcn_perm(r1[w], r0[w], sel);
-              val.y = __builtin_amdgcn_perm(r3[w], r2[w], sel);
-              const int d = dc * 8 + 2 * w + hh;
-              *(uint2*)(vs_ + d * C::VROW + 2 * pos) = val;
-            }
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
+            uint2 val;
+            val.x = __builtin_amdgcn_perm(r1[w], r0[w], sel);
+            val.y = __builtin_amdgcn_perm(r3[w], r2[w], sel);
+            const int d = dc * 8 + 2 * w + hh;
+            *(uint2*)(vs_ + d * C::VROW + 2 * pos) = val;
           }
         }
       }
@@ -271,22 +319,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
   };
 
   // ---- per-query running state ---------------------------------------------------
-  f32x16 oacc[QT][DV / 32];
-  float m_run[QT], l_run[QT], lx_run[QT];
+  f32x16 oacc[DV / 32];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-    lx_run[t] = 0.f;
+  for (int md = 0; md < DV / 32; ++md)
 #pragma unroll
-    for (int md = 0; md < DV / 32; ++md)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[t][md][i] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
+  float m_run = -INFINITY;   // running max (raw score units), same in both lane halves
+  float l_run = 0.f;         // row sum relative to m_run (FP8: of the rounded P, full row;
+                             // BF16: this lane's keys only)
+  float lx_run = 0.f;        // FP8 + LSE: exact row sum over this lane's keys
 
   const int wg_end = min(q0 + C::BM, N);
   const int n_kt = (wg_end + BN - 1) / BN;                 // tiles the workgroup loads
-  const int w_end = min(q0w + QT * 32, N);
+  const int w_end = min(q0w + 32, N);
   const int w_kt = q0w < N ? (w_end + BN - 1) / BN : 0;    // tiles this wave needs
 
   load_tile(0);
@@ -301,166 +346,133 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
       const char* ks_ = lds + buf * C::STAGE;
       const char* vs_ = ks_ + C::K_BYTES;
 
-      // S^T = K Q^T : two 32-key M-tiles x QT query N-tiles
-      f32x16 s[2][QT];
+      // S^T = K Q^T : MT 32-key M-tiles
+      f32x16 s[C::MT];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-        for (int t = 0; t < QT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[m][t][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[m][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < C::MT; ++m) {
           const char* rp = ks_ + (32 * m + l32) * C::KROW;
-          if (FP8) {
-            const uint4 a = *(const uint4*)(rp + 64 * ks + 32 * g);
-            const uint4 bb = *(const uint4*)(rp + 64 * ks + 32 * g + 16);
-            i32x8 kf;
-            kf[0] = a.x; kf[1] = a.y; kf[2] = a.z; kf[3] = a.w;
-            kf[4] = bb.x; kf[5] = bb.y; kf[6] = bb.z; kf[7] = bb.w;
-#pragma unroll
-            for (int t = 0; t < QT; ++t)
-              s[m][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  kf, *(i32x8*)&qf[t][ks], s[m][t], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+          if constexpr (FP8) {
+            const i32x8 kf = load_i32x8(rp + 64 * ks + 32 * g);
+            s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                kf, *(const i32x8*)&qf[ks], s[m], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
           } else {
             const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
-            const bf16x8 kf = *(const bf16x8*)&a;
-#pragma unroll
-            for (int t = 0; t < QT; ++t)
-              s[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, *(bf16x8*)&qf[t][ks],
-                                                                s[m][t], 0, 0, 0);
+            s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a,
+                                                           *(const bf16x8*)&qf[ks], s[m],
+                                                           0, 0, 0);
           }
         }
       }
 
       // causal mask on the tile(s) that cross this wave's diagonal
-      const bool diag = kt * BN + BN - 1 > q0w;
-      if (diag) {
+      if (kt * BN + BN - 1 > q0w) {
+        const int qrow = q0w + l32;
 #pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          const int qrow = q0w + 32 * t + l32;
+        for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kt * BN + 32 * m + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (key > qrow) s[m][t][i] = -INFINITY;
-            }
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt * BN + 32 * m + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > qrow) s[m][i] = -INFINITY;
+          }
       }
 
-      if (FP8) {
-        i32x8 pf[QT];
-        int psc[QT];
+      // max over each 64-key block (this lane's 32 keys, then the other lane half's)
+      float bmx[C::NB];
 #pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          float mx = -INFINITY;
+      for (int nb = 0; nb < C::NB; ++nb) {
+        bmx[nb] = -INFINITY;
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+        for (int e = 0; e < 32; ++e) bmx[nb] = fmaxf(bmx[nb], s[2 * nb + (e >> 4)][e & 15]);
+        if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
+      }
+      float mx = bmx[0];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[m][t][i]);
-          mx = fmaxf(mx, xor32(mx));
-          const float m_new = fmaxf(m_run[t], mx);
-          const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
-          m_run[t] = m_new;
-          // block exponent: block max 2^(x_max + k) in (2^7, 2^8]
-          const float xmax = (mx - m_new) * c;
+      for (int nb = 1; nb < C::NB; ++nb) mx = fmaxf(mx, bmx[nb]);
+      // lazy running max: rescale only when some row's tile max exceeds m by > TAU
+      if (__any((mx - m_run) * c > TAU)) {
+        const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+        if (WANT_LSE) lx_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+      }
+      const float nmc = -m_run * c;
+
+      if constexpr (FP8) {
+        const float A = 8.f * c;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          // one block exponent per query and 64-key block (both operand scale blocks)
+          const float xmax = fmaf(bmx[nb], c, nmc);
           const float kbf = fminf(floorf(8.f - xmax), 127.f);
-          const int kb = (int)kbf;
-          psc[t] = 127 - kb;
-          const float A = 8.f * c;
-          const float Bc = fmaf(-A, m_new, 8.f * kbf + LEANP_C0);
-          uint32_t w[8];
+          const int psc = 127 - (int)kbf;
+          const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
+          i32x8 pf;
 #pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            const float val = fmaf(s[e >> 4][t][e & 15], A, Bc);
-            const uint32_t old = (e & 3) ? w[e >> 2] : 0u;
-            w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(val, e & 3, old);
+          for (int w = 0; w < 8; ++w) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int e = 4 * w + j;
+              word = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc),
+                                                    j, word);
+            }
+            pf[w] = (int)word;
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[t][e] = (int)w[e];
           if (WANT_LSE) {
-            const float nmc = -m_new * c;
             float lx = 0.f;
 #pragma unroll
             for (int e = 0; e < 32; ++e)
-              lx += __builtin_amdgcn_exp2f(fmaf(s[e >> 4][t][e & 15], c, nmc));
-            lx_run[t] = lx_run[t] * alpha + lx;
+              lx += __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, nmc));
+            lx_run += lx;
           }
-          l_run[t] *= alpha;
+          // O^T += V^T P^T, block scale removed by the scaled MFMA
 #pragma unroll
-          for (int md = 0; md < DV / 32; ++md)
+          for (int md = 0; md < DV / 32; ++md) {
+            const i32x8 vf = load_i32x8(vs_ + (32 * md + l32) * C::VROW + 64 * nb + 32 * g);
+            oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                vf, pf, oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc);
+          }
+          // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
+          i32x8 ones;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[t][md][i] *= alpha;
-        }
-        // O^T += V^T P^T, block scale removed by the scaled MFMA
-#pragma unroll
-        for (int md = 0; md < DV / 32; ++md) {
-          const char* rp = vs_ + (32 * md + l32) * C::VROW + 32 * g;
-          const uint4 a = *(const uint4*)(rp);
-          const uint4 bb = *(const uint4*)(rp + 16);
-          i32x8 vf;
-          vf[0] = a.x; vf[1] = a.y; vf[2] = a.z; vf[3] = a.w;
-          vf[4] = bb.x; vf[5] = bb.y; vf[6] = bb.z; vf[7] = bb.w;
-#pragma unroll
-          for (int t = 0; t < QT; ++t)
-            oacc[t][md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                vf, pf[t], oacc[t][md], 0, 0, 0, 0x7f7f7f7f, 0, psc[t]);
-        }
-        // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
-        i32x8 ones;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
+          for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
           f32x16 z;
 #pragma unroll
           for (int i = 0; i < 16; ++i) z[i] = 0.f;
-          z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[t], z, 0, 0, 0,
-                                                              0x7f7f7f7f, 0, psc[t]);
-          l_run[t] += z[0];
+          z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, z, 0, 0, 0,
+                                                              0x7f7f7f7f, 0, psc);
+          l_run += z[0];
         }
       } else {
-        bf16x8 pf[QT][4];
+        bf16x8 pf[C::MT * 2];
+        float rs = 0.f;
 #pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[m][t][i]);
-          mx = fmaxf(mx, xor32(mx));
-          const float m_new = fmaxf(m_run[t], mx);
-          const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
-          m_run[t] = m_new;
-          const float nmc = -m_new * c;
-          float rs = 0.f;
-#pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][t][e & 15], c, nmc));
-            rs += pv;
-            pf[t][e >> 3][e & 7] = (__bf16)pv;
-          }
-          l_run[t] = l_run[t] * alpha + rs;
-#pragma unroll
-          for (int md = 0; md < DV / 32; ++md)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[t][md][i] *= alpha;
+        for (int e = 0; e < 16 * C::MT; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c, nmc));
+          rs += pv;
+          pf[e >> 3][e & 7] = (__bf16)pv;
         }
-        // O^T += V^T P^T over 4 k-steps of 16 keys
+        l_run += rs;
+        // O^T += V^T P^T over k-steps of 16 keys
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * C::MT; ++kk) {
 #pragma unroll
           for (int md = 0; md < DV / 32; ++md) {
             const uint4 a =
                 *(const uint4*)(vs_ + (32 * md + l32) * C::VROW + 2 * (16 * kk + 8 * g));
-            const bf16x8 vf = *(const bf16x8*)&a;
-#pragma unroll
-            for (int t = 0; t < QT; ++t)
-              oacc[t][md] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][kk], oacc[t][md], 0, 0, 0);
+            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a, pf[kk],
+                                                               oacc[md], 0, 0, 0);
           }
         }
       }
@@ -471,62 +483,52 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------
+  const int qrow = q0w + l32;
+  float l = l_run;
+  if (!FP8) l += xor32(l);
+  float lsum = l;
+  if (FP8 && WANT_LSE) lsum = lx_run + xor32(lx_run);
+  const float inv = (FP8 ? vds : 1.f) / l;
+  if (qrow < N) {
+    __bf16* orow = (__bf16*)p.o + ((size_t)(b * N + qrow) * p.Hq + h) * DV;
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int qrow = q0w + 32 * t + l32;
-    float l = l_run[t];
-    if (!FP8) l += xor32(l);
-    float lsum = l;
-    if (FP8 && WANT_LSE) lsum = lx_run[t] + xor32(lx_run[t]);
-    const float inv = (FP8 ? vds : 1.f) / l;
-    if (qrow < N) {
-      __bf16* orow = (__bf16*)p.o + ((size_t)(b * N + qrow) * p.Hq + h) * DV;
+    for (int md = 0; md < DV / 32; ++md)
 #pragma unroll
-      for (int md = 0; md < DV / 32; ++md)
+      for (int r = 0; r < 4; ++r) {
+        bf16x4 ov;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bf16x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[t][md][4 * r + e] * inv);
-          *(bf16x4*)(orow + 32 * md + 8 * r + 4 * g) = ov;
-        }
-      if (WANT_LSE && g == 0)
-        p.lse[((size_t)b * p.Hq + h) * N + qrow] =
-            (m_run[t] * c + __builtin_amdgcn_logf(lsum)) * LN2;
-    }
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[md][4 * r + e] * inv);
+        *(bf16x4*)(orow + 32 * md + 8 * r + 4 * g) = ov;
+      }
+    if (WANT_LSE && g == 0)
+      p.lse[((size_t)b * p.Hq + h) * N + qrow] =
+          (m_run * c + __builtin_amdgcn_logf(lsum)) * LN2;
   }
 }
 
-template <bool FP8, int DQK, int NW, int QT>
+template <bool FP8, int DQK, int BN, int NW>
 static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
-  using C = Cfg<FP8, DQK, NW, QT>;
+  using C = Cfg<FP8, DQK, BN, NW>;
   FwdParams p = p0;
   p.n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.lse) {
-    auto kern = attn_fwd_kernel<FP8, DQK, NW, QT, true>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
-  } else {
-    auto kern = attn_fwd_kernel<FP8, DQK, NW, QT, false>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
-  }
+  auto kern = p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, true>
+                    : attn_fwd_kernel<FP8, DQK, BN, NW, false>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream) {
   if (fp8) {
-    if (d_qk == 128) return launch_cfg<true, 128, 4, 2>(p, stream);
-    return launch_cfg<true, 192, 4, 2>(p, stream);
+    if (d_qk == 128) return launch_cfg<true, 128, 128, 4>(p, stream);
+    return launch_cfg<true, 192, 64, 4>(p, stream);
   }
-  if (d_qk == 128) return launch_cfg<false, 128, 4, 2>(p, stream);
-  return launch_cfg<false, 192, 4, 2>(p, stream);
+  if (d_qk == 128) return launch_cfg<false, 128, 64, 4>(p, stream);
+  return launch_cfg<false, 192, 64, 8>(p, stream);
 }
 
 }  // namespace attn

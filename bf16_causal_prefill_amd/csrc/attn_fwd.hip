@@ -81,7 +81,9 @@ struct Cfg {
   static constexpr int KCH = BN * R16;               // chunks per K tile
   static constexpr int KPT = (KCH + NT - 1) / NT;    // K chunks per thread
   static constexpr int VROW = BN * EB + 16;          // padded LDS row of V^T
-  static constexpr int VUN = (BN / 4) * (DV / 8);    // units of 4 keys x 8 channels
+  static constexpr int VCH = BN * EB / 16;           // 16-byte chunks per V^T row
+  static constexpr int VK = FP8 ? 8 : 4;             // keys per V copy unit
+  static constexpr int VUN = (BN / VK) * (DV / 8);   // units of VK keys x 8 channels
   static constexpr int VPT = (VUN + NT - 1) / NT;
   static constexpr int K_BYTES = BN * KROW;
   static constexpr int V_BYTES = DV * VROW;
@@ -93,16 +95,34 @@ struct Cfg {
   static_assert(BN % 64 == 0, "key tile must be a multiple of 64");
 };
 
-// Position of key `key` (0..BN-1) inside a V^T row of the LDS tile: the keys one lane
-// feeds to one P V MFMA become contiguous (see the file comment).  Works on groups of
-// 4 keys (kg = key / 4), which stay contiguous.
+// V^T key order.  Inside a row of the LDS V^T tile the keys are permuted so that the
+// keys one lane feeds to one P V MFMA are contiguous (see the file comment):
+//   FP8:  key 64n + 32m + 8a + 4g + b  sits at  64n + 32g + 16m + 4a + b
+//   BF16: key 16s + 8a + 4g + b        sits at  16s + 8g + 4a + b
+// A copy unit is a set of keys whose positions are contiguous: FP8 units hold 8 keys
+// (kbase + {0..3, 8..11}, 8 positions), BF16 units 4 keys (4 positions).
 template <bool FP8>
-__device__ __forceinline__ int vpos_of_group(int kg) {
-  if (FP8) {  // key = 64n + 32m + 8a + 4g + b  ->  64n + 32g + 16m + 4a + b
-    return 64 * (kg >> 4) + 32 * (kg & 1) + 16 * ((kg >> 3) & 1) + 4 * ((kg >> 1) & 3);
-  } else {    // key = 16s + 8a + 4g + b  ->  16s + 8g + 4a + b
-    return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-  }
+__device__ __forceinline__ int vunit_key0(int ku) {
+  if (FP8) return 64 * (ku >> 3) + 32 * ((ku >> 2) & 1) + 16 * ((ku >> 1) & 1) + 4 * (ku & 1);
+  return 4 * ku;
+}
+template <bool FP8>
+__device__ __forceinline__ int vunit_key(int ku, int j) {   // j-th key of unit ku
+  if (FP8) return vunit_key0<true>(ku) + (j & 3) + 8 * (j >> 2);
+  return 4 * ku + j;
+}
+template <bool FP8>
+__device__ __forceinline__ int vunit_pos(int ku) {          // first position of unit ku
+  if (FP8) return 64 * (ku >> 3) + 32 * (ku & 1) + 16 * ((ku >> 2) & 1) + 8 * ((ku >> 1) & 1);
+  return 16 * (ku >> 2) + 8 * (ku & 1) + 4 * ((ku >> 1) & 1);
+}
+
+// Byte offset of logical byte x of V^T row `row`: the row's 16-byte chunks are
+// XOR-swizzled by (row / 16), so the 16 lanes that store the same positions of 16
+// different 8-channel groups hit different LDS banks.
+template <int VCH>
+__device__ __forceinline__ int vswz(int row, int x) {
+  return (((x >> 4) ^ ((row >> 4) & (VCH - 1))) << 4) | (x & 15);
 }
 
 // Maps the flat workgroup id to (batch, query head, query tile).  Heaviest causal
@@ -211,8 +231,8 @@ void attn_fwd_kernel(FwdParams p) {
   // zeros (they are masked: key > every query row).
   uint4 kreg[C::KPT];
   typedef typename std::conditional<FP8, uint2, uint4>::type VLoad;
-  VLoad vreg[C::VPT][4];
-  uint32_t koff[C::KPT], voff[C::VPT][4];
+  VLoad vreg[C::VPT][C::VK];
+  uint32_t koff[C::KPT], voff[C::VPT][C::VK];
 #pragma unroll
   for (int cix = 0; cix < C::KPT; ++cix) {
     const int cc = tid + cix * C::NT;
@@ -222,10 +242,11 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int u = 0; u < C::VPT; ++u) {
     const int uu = tid + u * C::NT;
-    const int dc = uu & 15, kg = uu >> 4;
+    const int dc = uu & 15, ku = uu >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      voff[u][j] = (uint32_t)(4 * kg + j) * (uint32_t)vstride + (uint32_t)(dc * 8 * C::EB);
+    for (int j = 0; j < C::VK; ++j)
+      voff[u][j] = (uint32_t)vunit_key<FP8>(ku, j) * (uint32_t)vstride +
+                   (uint32_t)(dc * 8 * C::EB);
   }
 
   auto load_tile = [&](int kt) {
@@ -246,7 +267,7 @@ void attn_fwd_kernel(FwdParams p) {
     for (int u = 0; u < C::VPT; ++u) {
       if (C::VUN % C::NT != 0 && tid + u * C::NT >= C::VUN) break;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < C::VK; ++j) {
         if constexpr (FP8) {
           const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, voff[u][j], 0, 0);
           vreg[u][j] = *(const VLoad*)&x;
@@ -272,29 +293,34 @@ void attn_fwd_kernel(FwdParams p) {
     for (int u = 0; u < C::VPT; ++u) {
       const int uu = tid + u * C::NT;
       if (C::VUN % C::NT != 0 && uu >= C::VUN) break;
-      const int dc = uu & 15, kg = uu >> 4;
-      const int pos = vpos_of_group<FP8>(kg);
+      const int dc = uu & 15, ku = uu >> 4;
+      const int pos = vunit_pos<FP8>(ku);
       if constexpr (FP8) {
-        // 4 keys x 8 channels of bytes -> 8 rows (channels) of 4 key bytes.
+        // 8 keys x 8 channels of bytes -> 8 rows (channels) of 8 key bytes.
+        uint32_t wd[2][8];
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const uint32_t a0 = w ? vreg[u][0].y : vreg[u][0].x;
-          const uint32_t a1 = w ? vreg[u][1].y : vreg[u][1].x;
-          const uint32_t a2 = w ? vreg[u][2].y : vreg[u][2].x;
-          const uint32_t a3 = w ? vreg[u][3].y : vreg[u][3].x;
-          const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-          const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-          const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-          const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-          const uint32_t o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-          const uint32_t o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-          const uint32_t o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-          const uint32_t o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-          const int d0 = dc * 8 + 4 * w;
-          *(uint32_t*)(vs_ + (d0 + 0) * C::VROW + pos) = o0;
-          *(uint32_t*)(vs_ + (d0 + 1) * C::VROW + pos) = o1;
-          *(uint32_t*)(vs_ + (d0 + 2) * C::VROW + pos) = o2;
-          *(uint32_t*)(vs_ + (d0 + 3) * C::VROW + pos) = o3;
+        for (int h4 = 0; h4 < 2; ++h4) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t a0 = w ? vreg[u][4 * h4 + 0].y : vreg[u][4 * h4 + 0].x;
+            const uint32_t a1 = w ? vreg[u][4 * h4 + 1].y : vreg[u][4 * h4 + 1].x;
+            const uint32_t a2 = w ? vreg[u][4 * h4 + 2].y : vreg[u][4 * h4 + 2].x;
+            const uint32_t a3 = w ? vreg[u][4 * h4 + 3].y : vreg[u][4 * h4 + 3].x;
+            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+            wd[h4][4 * w + 0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+            wd[h4][4 * w + 1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+            wd[h4][4 * w + 2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+            wd[h4][4 * w + 3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int row = dc * 8 + r;
+          *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, pos)) =
+              make_uint2(wd[0][r], wd[1][r]);
         }
       } else {
         // 4 keys x 8 channels of bf16 -> 8 rows (channels) of 4 keys (8 bytes).
@@ -310,8 +336,8 @@ void attn_fwd_kernel(FwdParams p) {
             uint2 val;
             val.x = __builtin_amdgcn_perm(r1[w], r0[w], sel);
             val.y = __builtin_amdgcn_perm(r3[w], r2[w], sel);
-            const int d = dc * 8 + 2 * w + hh;
-            *(uint2*)(vs_ + d * C::VROW + 2 * pos) = val;
+            const int row = dc * 8 + 2 * w + hh;
+            *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, 2 * pos)) = val;
           }
         }
       }
@@ -416,43 +442,66 @@ void attn_fwd_kernel(FwdParams p) {
           const float xmax = fmaf(bmx[nb], c, nmc);
           const float kbf = fminf(floorf(8.f - xmax), 127.f);
           const int psc = 127 - (int)kbf;
-          const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
           i32x8 pf;
+          if constexpr (WANT_LSE) {
+            // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
+            // fp32 sum (scale removed) normalises O and gives the log-sum-exp
+            const float off = nmc + kbf;
+            float bs = 0.f;
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            uint32_t word = 0u;
+            for (int w = 0; w < 8; ++w) {
+              float pv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 4 * w + j;
-              word = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc),
-                                                    j, word);
+              for (int j = 0; j < 4; ++j) {
+                const int e = 4 * w + j;
+                pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
+                bs += pv[j];
+              }
+              int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+              pf[w] = word;
             }
-            pf[w] = (int)word;
-          }
-          if (WANT_LSE) {
-            float lx = 0.f;
+            lx_run += __builtin_ldexpf(bs, -(int)kbf);
+          } else {
+            // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
+            const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
 #pragma unroll
-            for (int e = 0; e < 32; ++e)
-              lx += __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, nmc));
-            lx_run += lx;
+            for (int w = 0; w < 8; ++w) {
+              uint32_t word = 0u;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int e = 4 * w + j;
+                word = __builtin_amdgcn_cvt_pk_u8_f32(
+                    fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc), j, word);
+              }
+              pf[w] = (int)word;
+            }
           }
           // O^T += V^T P^T, block scale removed by the scaled MFMA
 #pragma unroll
           for (int md = 0; md < DV / 32; ++md) {
-            const i32x8 vf = load_i32x8(vs_ + (32 * md + l32) * C::VROW + 64 * nb + 32 * g);
+            const int row = 32 * md + l32;
+            const char* rp = vs_ + row * C::VROW;
+            const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g));
+            const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g + 16));
+            i32x8 vf;
+            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
+            vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
             oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 vf, pf, oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc);
           }
-          // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
-          i32x8 ones;
+          if constexpr (!WANT_LSE) {
+            // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
+            i32x8 ones;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
-          f32x16 z;
+            for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
+            f32x16 z;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = 0.f;
-          z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, z, 0, 0, 0,
-                                                              0x7f7f7f7f, 0, psc);
-          l_run += z[0];
+            for (int i = 0; i < 16; ++i) z[i] = 0.f;
+            z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, z, 0, 0, 0,
+                                                                0x7f7f7f7f, 0, psc);
+            l_run += z[0];
+          }
         }
       } else {
         bf16x8 pf[C::MT * 2];
@@ -469,8 +518,9 @@ void attn_fwd_kernel(FwdParams p) {
         for (int kk = 0; kk < 2 * C::MT; ++kk) {
 #pragma unroll
           for (int md = 0; md < DV / 32; ++md) {
-            const uint4 a =
-                *(const uint4*)(vs_ + (32 * md + l32) * C::VROW + 2 * (16 * kk + 8 * g));
+            const int row = 32 * md + l32;
+            const uint4 a = *(const uint4*)(vs_ + row * C::VROW +
+                                            vswz<C::VCH>(row, 2 * (16 * kk + 8 * g)));
             oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a, pf[kk],
                                                                oacc[md], 0, 0, 0);
           }
@@ -486,8 +536,8 @@ void attn_fwd_kernel(FwdParams p) {
   const int qrow = q0w + l32;
   float l = l_run;
   if (!FP8) l += xor32(l);
-  float lsum = l;
-  if (FP8 && WANT_LSE) lsum = lx_run + xor32(lx_run);
+  if (FP8 && WANT_LSE) l = lx_run + xor32(lx_run);
+  const float lsum = l;
   const float inv = (FP8 ? vds : 1.f) / l;
   if (qrow < N) {
     __bf16* orow = (__bf16*)p.o + ((size_t)(b * N + qrow) * p.Hq + h) * DV;

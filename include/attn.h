@@ -77,13 +77,18 @@ int attn_fwd_causal_bf16(const void* q, const void* k, const void* v,
  *             when descale_per_head == 0, else Hq (q) / Hkv (k, v) values.
  *   o, lse    as for the BF16 entry point (o is bf16).
  * Q.K^T and P.V run on the e4m3 matrix instructions with float32
- * accumulation.  Each probability is written straight as an e4m3 code from
- * one multiply-add and one integer conversion, using that the code of 2^x is
- * about 8x plus a constant; each 64-key block of probabilities is scaled by a
- * power of two that the scaled matrix instruction removes, and O is divided
- * by the sum of the rounded probabilities.  When lse != NULL the log-sum-exp
- * comes from a separate float32 sum of exact exponentials (the rounded sum is
- * too coarse for it); lse == NULL skips that work.
+ * accumulation; each 64-key block of probabilities is scaled by a power of two
+ * that the scaled matrix instruction removes.
+ *   lse == NULL: each probability is written straight as an e4m3 code from one
+ *             multiply-add and one integer conversion, using that the code of 2^x
+ *             is about 8x plus a constant, and O is divided by the sum of the
+ *             rounded probabilities (one extra matrix instruction per block).
+ *   lse != NULL: the probabilities are exact exponentials rounded to e4m3, and
+ *             their exact float32 sum both normalises O and gives the LSE (the
+ *             rounded-code sum is too coarse for an LSE).
+ * The FP8 matrix instructions sum each run of 8 products after aligning them to
+ * the largest, keeping about 12 bits below it, so scores carry an error of up to
+ * 7 * 2^-12 * max|q_c k_c| per 8 channels; O and LSE inherit it.
  */
 int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
                         const float* q_descale, const float* k_descale,

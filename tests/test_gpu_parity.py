@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_harness import (bf16_bytes, check, gpu_quantize, note, run_bf16, run_fp8)
+from gpu_harness import (bf16_bytes, check, fp8_score_error_bound, gpu_quantize, note,
+                         run_bf16, run_fp8)
 
 pytestmark = pytest.mark.gpu
 
@@ -79,24 +80,50 @@ def test_fp8_parity_full(case):
     (qc, qd), (kc, kd), (vc, vd) = dev
     out = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale)[0]
     ro, rl = oracle.causal_attention(q, k, v, w.softmax_scale)
-    check(case, "fp8", out.o, ro, out.lse, rl)
+    check(case, "fp8", out.o, ro, out.lse, rl, lse_bound=_outlier_bound(w, q, k, rl.shape))
+
+
+def _outlier_bound(w, q, k, lse_shape, rows=None):
+    """Accumulation-error allowance for the FP8 LSE, only on the outlier-channel
+    workloads (lognormal channel spread with x20 outliers); None elsewhere, so the
+    plain 1e-2 gate applies."""
+    if w.recipe != "mistral":
+        return None
+
+    def bound(flat):
+        if rows is None:
+            idx = [tuple(int(t) for t in np.unravel_index(f, lse_shape)) for f in flat]
+        else:
+            idx = [rows[int(f)] for f in flat]
+        # lse is (B, Hq, N); the bound wants (b, h, i)
+        return fp8_score_error_bound(q, k, w.softmax_scale, idx)
+    return bound
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp8"])
-def test_without_lse_same_output(prec):
-    """lse=NULL skips the LSE work but leaves O unchanged (byte-identical)."""
+def test_without_lse(prec):
+    """lse=NULL skips the LSE work.  BF16: O is byte-identical to the LSE run.
+    FP8: without the LSE the kernel writes the probabilities with the one-FMA
+    e4m3 code and normalises by the row sum of the rounded codes (a different,
+    cheaper approximation than the LSE run's exact exponentials), so O is checked
+    against the oracle on its own, within the FP8 tolerance."""
     w = SMALL["ragged_gqa_n300_b2"]
     x = workloads.generate(w)
     if prec == "bf16":
         (qu, ku, vu), _ = _oracle_bf16(x, w)
         a = run_bf16(qu, ku, vu, w.softmax_scale, want_lse=True)[0]
         b = run_bf16(qu, ku, vu, w.softmax_scale, want_lse=False)[0]
+        assert a.o_bytes == b.o_bytes
     else:
-        dev, _ = _fp8_inputs(x, w)
-        (qc, qd), (kc, kd), (vc, vd) = dev
-        a = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, want_lse=True)[0]
-        b = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, want_lse=False)[0]
-    assert a.o_bytes == b.o_bytes
+        for case in ("ragged_gqa_n300_b2", "mistral_n1024", "mla_n700"):
+            w = SMALL[case]
+            x = workloads.generate(w)
+            dev, (q, k, v) = _fp8_inputs(x, w)
+            (qc, qd), (kc, kd), (vc, vd) = dev
+            b = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale,
+                        want_lse=False)[0]
+            ro, _ = oracle.causal_attention(q, k, v, w.softmax_scale)
+            check(case + "/no-lse", "fp8", b.o, ro)
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp8"])
@@ -225,4 +252,27 @@ def test_full_size_sampled_rows(name, prec):
     go = out.o[bb, ii, hh]
     gl = out.lse[bb, hh, ii]
     assert np.all(np.isfinite(out.o)) and np.all(np.isfinite(out.lse))
-    check(f"{name}/rows", prec, go, ro, gl, rl)
+    lb = _outlier_bound(w, q, k, gl.shape, rows) if prec == "fp8" else None
+    check(f"{name}/rows", prec, go, ro, gl, rl, lse_bound=lb)
+
+
+def test_fp8_matrix_accumulation_model():
+    """Pins the accumulation behaviour the FP8 LSE allowance relies on, through the
+    C ABI.  With N = 1 the LSE of row 0 is its single score q.k (scale 1, unit
+    descales).  q = [256, 1 x 15, 0...], k = [64, 1 x 15, 0...]: the exact dot product
+    is 16384 + 15 = 16399.  The 7 unit products that share the 8-channel group of the
+    2^14 product fall below 2^(14-12) and are dropped; the 8 in the next group are
+    kept, so the hardware gives 16392."""
+    dev = "cuda:0"
+    qc = np.zeros((1, 1, 1, 128), np.uint8)
+    kc = np.zeros((1, 1, 1, 128), np.uint8)
+    qc[..., 0], kc[..., 0] = 0x78, 0x68          # e4m3 256 and 64
+    qc[..., 1:16], kc[..., 1:16] = 0x38, 0x38    # e4m3 1.0
+    vc = np.full((1, 1, 1, 128), 0x38, np.uint8)
+    one = torch.ones(1, device=dev)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    out = run_fp8(t(qc), t(kc), t(vc), one, one, one, False, 1.0)[0]
+    lse0 = float(out.lse[0, 0, 0])
+    note(f"fp8 accumulation pin: lse0={lse0} (exact 16399, grouped model 16392)")
+    assert abs(lse0 - 16392.0) < 0.5
+    assert np.all(out.o == 1.0)

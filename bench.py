@@ -1,18 +1,23 @@
 """Benchmark of the causal prefill attention hot path on one MI355X.
 
 One step = the whole FP8 path over one batch of the "gauss32k" workload
-(B=1, Hq=32, Hkv=8, N=32768, d=128, iid N(0,1) inputs already resident in
-HBM as float32): quantize_e4m3 of Q, K and V (per-tensor scales), then
-attn_fwd_causal_fp8 writing O (bf16) and the LSE.  `value` is causal TFLOP/s
-of that step, counting only the attention FLOPs 4*B*Hq*N^2*d/2.
+(B=1, Hq=32, Hkv=8, N=32768, d=128, iid N(0,1) inputs already resident in HBM
+as float32): quantize_e4m3 of Q, K and V (per-tensor scales), then
+attn_fwd_causal_fp8 writing O (bf16) and the LSE (fp32).  `value` is the causal
+TFLOP/s of that step, counting only the attention FLOPs 4*B*Hq*N^2*d/2.
 
-Also printed (in "extra"): the attention kernels alone, FP8 with and without
-the LSE, BF16, and the MLA shape at 32K, each timed with HIP events on the
-stream the kernels run on.  `roofline` is for the dominant kernel (the FP8
-attention kernel): achieved = algorithmic FLOPs per launch / its mean launch
-time; `cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+`roofline` describes the dominant kernel (the FP8 attention kernel): achieved =
+its algorithmic FLOPs per launch / its mean launch time, measured with HIP
+events on the stream the library launches on, over the timed steps; peak = the
+MI355X dense FP8 matrix peak; traffic = HBM bytes per launch from the committed
+rocprofv3 counter summary when it was taken on the current kernel source, else
+null.  `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.  "extra" holds the other precisions and shapes of the metric (FP8 with
+and without the LSE, BF16, the MLA shape at 32K) timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+       python bench.py --profile-only [--steps K]   (step loop only, for rocprofv3)
+       python bench.py --copy-only MIB              (plain device copy, counter calibration)
 """
 from __future__ import annotations
 
@@ -20,71 +25,48 @@ import argparse
 import hashlib
 import json
 import os
-import subprocess
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal prefill attn TFLOP/s @32K (FP8/BF16, d128 & MLA); % MFMA peak"
-PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}   # MI355X dense MFMA peaks
-PAGES_FP8_D128_32K = 2672.0                      # the pages' figure (context)
+# MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x 8192 (fp8) / 4096 (bf16).
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+PAGES_FP8_D128_32K = 2672.0   # the pages' MI355X figure (B, H unstated): context only
+KERNEL_SOURCES = ("attn_fwd.hip", "kernels.h")
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-class ClockPoller:
-    """Samples the GPU shader clock with amd-smi while the timed loop runs."""
+def kernel_source_sha() -> str:
+    """Hash of the attention kernel sources; the committed counter summary is
+    used only when it was taken on exactly these sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bf16_causal_prefill_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
-    def __init__(self, period: float = 0.05):
-        self.period = period
-        self.samples: list[float] = []
-        self._stop = threading.Event()
-        self._t = None
 
-    def _read(self) -> float | None:
-        try:
-            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"],
-                               capture_output=True, text=True, timeout=5)
-            data = json.loads(r.stdout)
-            if isinstance(data, list):
-                data = data[0]
-            clk = data.get("clock", data)
-            gfx = clk.get("gfx_0") or clk.get("GFX_0") or {}
-            val = gfx.get("clk")
-            if isinstance(val, dict):
-                val = val.get("value")
-            return float(val) if val not in (None, "N/A") else None
-        except Exception:
+def traffic_from_profile(tag: str):
+    """HBM bytes per launch of kernel `tag` from profiles/traffic.json, or None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            ent = json.load(f)[tag]
+        if ent.get("source_sha") != kernel_source_sha():
             return None
-
-    def _run(self):
-        while not self._stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        self._t = threading.Thread(target=self._run, daemon=True)
-        self._t.start()
-        return self
-
-    def __exit__(self, *a):
-        self._stop.set()
-        self._t.join(timeout=10)
-
-    def mean(self):
-        return sum(self.samples) / len(self.samples) if self.samples else None
+        return ent["hbm_bytes_per_launch"]
+    except Exception:
+        return None
 
 
-def time_events(fn, iters: int, warmup: int = 2):
-    """Mean duration (ms) of fn() over `iters` launches, from HIP events on the
-    current stream (the stream the library launches on)."""
+def time_events(fn, iters: int, warmup: int = 2) -> float:
+    """Mean duration (ms) of fn() from HIP events on torch's current stream,
+    which is the stream the library launches on."""
     import torch
     for _ in range(warmup):
         fn()
@@ -99,32 +81,10 @@ def time_events(fn, iters: int, warmup: int = 2):
     return sum(a.elapsed_time(b) for a, b in evs) / iters
 
 
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "bf16_causal_prefill_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_from_profile(kernel_tag: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            data = json.load(f)
-        ent = data[kernel_tag]
-        if ent.get("source_sha") != kernel_source_sha():
-            return None
-        return ent["hbm_bytes_per_launch"]
-    except Exception:
-        return None
-
-
 def cpu_baseline(w, x, n_heads: int):
-    """fp64 oracle on the first `n_heads` query heads (all N rows) of the
-    workload's e4m3-decoded inputs; returns the baseline object."""
+    """The fp64 oracle on query heads 0..n_heads-1 (all N rows) of the workload's
+    e4m3-decoded inputs (per-tensor descales from the whole tensors).  Only the
+    attention itself is timed; the throughput counts the sample's causal FLOPs."""
     import numpy as np
     import oracle
     try:
@@ -135,20 +95,32 @@ def cpu_baseline(w, x, n_heads: int):
     G = w.Hq // w.Hkv
     n_kv = (n_heads + G - 1) // G
     dec = {}
-    for n in "qkv":
-        codes, ds = oracle.quantize_e4m3(x[n], per_head=w.fp8_per_head)
-        dsb = ds[None, None, :, None] if w.fp8_per_head else ds[0]
-        sl = slice(0, n_heads) if n == "q" else slice(0, n_kv)
-        dec[n] = oracle.e4m3_decode(codes[:, :, sl]) * (dsb[:, :, sl] if w.fp8_per_head else dsb)
+    for n, hs in (("q", n_heads), ("k", n_kv), ("v", n_kv)):
+        ds = oracle.absmax_descale(x[n], per_head=False)
+        codes = oracle.encode_with_descale(x[n][:, :, :hs], ds[0])
+        dec[n] = oracle.e4m3_decode(codes) * float(ds[0])
     t0 = time.perf_counter()
     oracle.causal_attention(dec["q"], dec["k"], dec["v"], w.softmax_scale)
     dt = time.perf_counter() - t0
     flops = 2.0 * w.B * n_heads * float(w.N) ** 2 * (w.d_qk + w.d_v) / 2.0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{w.name}: query heads 0..{n_heads - 1} of {w.Hq} (KV heads 0..{n_kv - 1}), "
-                      f"all {w.N} rows, e4m3-decoded inputs in float64; "
-                      f"throughput scaled by the sample's causal FLOPs"}
+            "sample": f"{w.name}: query heads 0..{n_heads - 1} of {w.Hq} (KV heads "
+                      f"0..{n_kv - 1}), all {w.N} rows, e4m3-decoded inputs in float64, "
+                      f"O and LSE; TFLOP/s = the sample's causal FLOPs / oracle seconds"}
+
+
+def copy_only(mib: int, reps: int = 3) -> int:
+    """A plain device-to-device copy of `mib` MiB, for calibrating the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) against a known size."""
+    import torch
+    src = torch.ones(mib << 18, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copied {mib} MiB x {reps}")
+    return 0
 
 
 def main() -> int:
@@ -159,16 +131,20 @@ def main() -> int:
     ap.add_argument("--workload", default="gauss32k")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--profile-only", action="store_true",
                     help="run the step loop only (for rocprofv3), no JSON line")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: the kernels take one GPU's share of the "
-              "work and no figure at several GPUs is produced (use --gpus 1)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the attention kernels take one GPU's share "
+              "of the work and no figure at several GPUs is produced; run with --gpus 1",
+              file=sys.stderr)
         return 2
+    if args.copy_only:
+        return copy_only(args.copy_only)
 
-    import numpy as np
     import torch
     import bf16_causal_prefill_amd as ba
     import workloads
@@ -214,13 +190,12 @@ def main() -> int:
     torch.cuda.synchronize()
     ev_attn.clear()
     log(f"bench: timing {args.steps} steps")
-    with ClockPoller() as clk:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     if args.profile_only:
         log("bench: profile-only run done")
         return 0
@@ -231,25 +206,23 @@ def main() -> int:
     log(f"bench: step {ms_step:.3f} ms ({value:.1f} TFLOP/s); fp8 attention {attn_ms:.3f} ms "
         f"({achieved:.1f} TFLOP/s)")
 
-    extra = {}
+    extra = {"fp8_attn_lse_ms": round(attn_ms, 4)}
     if not args.no_extra:
-        extra["fp8_attn_lse_ms"] = round(attn_ms, 4)
         t = time_events(lambda: attn_fp8(False), 10)
         extra["fp8_attn_nolse_ms"] = round(t, 4)
         extra["fp8_attn_nolse_tflops"] = round(flops / t / 1e9, 1)
         t = time_events(quant, 10)
+        qbytes = sum(x[n].nbytes * 2 + x[n].size for n in "qkv")   # 2 reads + code write
         extra["quantize_qkv_ms"] = round(t, 4)
-        qbytes = sum(x[n].nbytes * 2 + x[n].size for n in "qkv")  # 2 reads + code write
         extra["quantize_qkv_GBps"] = round(qbytes / t / 1e6, 1)
-        # BF16 on the same workload
         xb = {n: xd[n].to(torch.bfloat16) for n in "qkv"}
-        t = time_events(lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, lse,
-                                                        softmax_scale=w.softmax_scale), 10)
-        extra["bf16_attn_ms"] = round(t, 4)
-        extra["bf16_attn_tflops"] = round(flops / t / 1e9, 1)
-        extra["bf16_pct_peak"] = round(100 * flops / t / 1e9 / PEAK_TFLOPS["bf16"], 2)
+        for tag, L in (("bf16_attn_lse", lse), ("bf16_attn_nolse", None)):
+            t = time_events(lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, L,
+                                                            softmax_scale=w.softmax_scale), 10)
+            extra[tag + "_tflops"] = round(flops / t / 1e9, 1)
+        extra["bf16_attn_lse_pct_peak"] = round(
+            100 * extra["bf16_attn_lse_tflops"] / PEAK_TFLOPS["bf16"], 2)
         del xb
-        # MLA shape at 32K
         wm = workloads.get("mla32k")
         log("bench: generating mla32k inputs")
         xm = workloads.generate(wm)
@@ -261,20 +234,15 @@ def main() -> int:
         dm = {n: torch.empty(xm[n].shape[2], device=dev) for n in "qkv"}
         for n in "qkv":
             ba.quantize_e4m3(xmd[n], cm[n], dm[n], per_head=True)
-        t = time_events(lambda: ba.attn_fwd_causal_fp8(cm["q"], cm["k"], cm["v"], dm["q"],
-                                                       dm["k"], dm["v"], om, lm,
-                                                       softmax_scale=wm.softmax_scale,
-                                                       descale_per_head=1), 10)
-        extra["mla32k_fp8_attn_tflops"] = round(fm / t / 1e9, 1)
-        t = time_events(lambda: ba.attn_fwd_causal_fp8(cm["q"], cm["k"], cm["v"], dm["q"],
-                                                       dm["k"], dm["v"], om, None,
-                                                       softmax_scale=wm.softmax_scale,
-                                                       descale_per_head=1), 10)
-        extra["mla32k_fp8_attn_nolse_tflops"] = round(fm / t / 1e9, 1)
+        for tag, L in (("mla32k_fp8_attn_lse", lm), ("mla32k_fp8_attn_nolse", None)):
+            t = time_events(lambda: ba.attn_fwd_causal_fp8(
+                cm["q"], cm["k"], cm["v"], dm["q"], dm["k"], dm["v"], om, L,
+                softmax_scale=wm.softmax_scale, descale_per_head=1), 10)
+            extra[tag + "_tflops"] = round(fm / t / 1e9, 1)
         xmb = {n: xmd[n].to(torch.bfloat16) for n in "qkv"}
         t = time_events(lambda: ba.attn_fwd_causal_bf16(xmb["q"], xmb["k"], xmb["v"], om, lm,
                                                         softmax_scale=wm.softmax_scale), 10)
-        extra["mla32k_bf16_attn_tflops"] = round(fm / t / 1e9, 1)
+        extra["mla32k_bf16_attn_lse_tflops"] = round(fm / t / 1e9, 1)
         del xmd, xmb, cm
 
     cpu = None
@@ -282,7 +250,6 @@ def main() -> int:
         log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
         cpu = cpu_baseline(w, x, args.cpu_heads)
 
-    sclk = clk.mean()
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -293,20 +260,20 @@ def main() -> int:
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_FP8_D128_32K, 4),
+        "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
-                   "d_qk": w.d_qk, "d_v": w.d_v,
-                   "step": "quantize_e4m3(q,k,v) + attn_fwd_causal_fp8 (O + LSE)",
-                   "parallelism": "single GPU"},
+                   "d_qk": w.d_qk, "d_v": w.d_v, "inputs": "iid N(0,1) float32 in HBM",
+                   "step": "quantize_e4m3(q,k,v) per tensor + attn_fwd_causal_fp8 (O + LSE)"},
         "pct_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
-        "sclk_mhz": round(sclk, 1) if sclk else None,
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<fp8,d128>",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<fp8, d128> (with LSE)",
                      "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp8"], 4),
-                     "traffic": traffic_from_profile("attn_fwd_fp8_d128_gauss32k")},
+                     "traffic": traffic_from_profile("attn_fwd_fp8_d128_lse_gauss32k")},
         "cpu_baseline": cpu,
+        "context": {"pages_fp8_d128_32k_tflops": PAGES_FP8_D128_32K,
+                    "note": "the pages' MI355X kernel figure; B, H and LSE handling unstated"},
         "extra": extra,
     }
     print(json.dumps(rec), flush=True)

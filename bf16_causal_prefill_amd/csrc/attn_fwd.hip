@@ -88,11 +88,13 @@ struct Cfg {
   static constexpr int K_BYTES = BN * KROW;
   static constexpr int V_BYTES = DV * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int LDS = 2 * STAGE;              // double buffered
+  static constexpr int NSTAGE = 3;                   // K/V tiles resident at once
+  static constexpr int LDS = NSTAGE * STAGE;
   static constexpr int KS = FP8 ? DQK / 64 : DQK / 16;  // MFMA k-steps of Q K^T
   static constexpr int MT = BN / 32;                 // 32-key M-tiles of S^T
   static constexpr int NB = BN / 64;                 // 64-key blocks
   static_assert(BN % 64 == 0, "key tile must be a multiple of 64");
+  static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
 };
 
 // V^T key order.  Inside a row of the LDS V^T tile the keys are permuted so that the
@@ -178,7 +180,7 @@ void attn_fwd_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -225,10 +227,8 @@ void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- K/V tile staging: global -> registers -> LDS (double buffered) -----------
-  // Buffer loads: each thread copies the same byte offsets of every tile, the tile's
-  // base address goes into the (uniform) buffer descriptor, and the descriptor's range
-  // ends at key N-1 of this sequence, so the keys past N in the last tile read as
-  // zeros (they are masked: key > every query row).
+  // Buffer loads: each thread copies the same byte offsets of every tile; keys past N
+  // in the last tile read as zeros (they are masked: key > every query row).
   uint4 kreg[C::KPT];
   typedef typename std::conditional<FP8, uint2, uint4>::type VLoad;
   VLoad vreg[C::VPT][C::VK];
@@ -249,18 +249,21 @@ void attn_fwd_kernel(FwdParams p) {
                    (uint32_t)(dc * 8 * C::EB);
   }
 
+  // One descriptor per tensor for the whole key range of this (b, kv head); a tile is
+  // addressed by adding its byte offset to the per-thread offsets.  The range ends at
+  // key N-1, so the last tile's keys past N read as zeros.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, (short)0, (N - 1) * (int)kstride + C::KRB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, (short)0, (N - 1) * (int)vstride + DV * C::EB, 0x00020000);
+
   auto load_tile = [&](int kt) {
-    const int keys_left = N - kt * BN;   // >= 1
-    const int kbytes = (keys_left - 1) * (int)kstride + C::KRB;
-    const int vbytes = (keys_left - 1) * (int)vstride + DV * C::EB;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (size_t)kt * BN * kstride), (short)0, kbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (size_t)kt * BN * vstride), (short)0, vbytes, 0x00020000);
+    const uint32_t kt_off = (uint32_t)kt * BN * (uint32_t)kstride;
+    const uint32_t vt_off = (uint32_t)kt * BN * (uint32_t)vstride;
 #pragma unroll
     for (int cix = 0; cix < C::KPT; ++cix) {
       if (C::KCH % C::NT != 0 && tid + cix * C::NT >= C::KCH) break;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[cix], 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(krsrc, koff[cix] + kt_off, 0, 0);
       kreg[cix] = *(const uint4*)&x;
     }
 #pragma unroll
@@ -269,10 +272,10 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < C::VK; ++j) {
         if constexpr (FP8) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vr, voff[u][j], 0, 0);
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff[u][j] + vt_off, 0, 0);
           vreg[u][j] = *(const VLoad*)&x;
         } else {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[u][j], 0, 0);
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff[u][j] + vt_off, 0, 0);
           vreg[u][j] = *(const VLoad*)&x;
         }
       }
@@ -360,20 +363,79 @@ void attn_fwd_kernel(FwdParams p) {
   const int w_end = min(q0w + 32, N);
   const int w_kt = q0w < N ? (w_end + BN - 1) / BN : 0;    // tiles this wave needs
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // ---- ping-pong main loop ----------------------------------------------------------
+  // The tile loop alternates a matrix phase, MFMA(t) = S(t) = K_t Q^T plus O += P(t-1)
+  // V_(t-1), with a softmax phase, VALU(t), which turns S(t) into P(t) (P V is thus
+  // software-pipelined by one tile).  Waves 0..3 (group A) and 4..7 (group B), one of
+  // each per SIMD, run the same sequence half a phase apart, separated by workgroup
+  // barriers: while one group issues matrix instructions the other does its softmax
+  // arithmetic on the same SIMD, and the matrix group runs at raised issue priority.
+  // Tiles are staged three deep in LDS: tile t+1 is written during MFMA(t), tile t is
+  // read by both groups' S(t) and P(t) V_t, which end before tile t+3 overwrites it.
+  const bool grp_b = wave >= NW / 2;
+  f32x16 s[C::MT];
+  i32x8 pf8[C::NB];             // FP8 P(t-1) operand, one per 64-key block
+  int psc[C::NB];               // its E8M0 block scales
+  bf16x8 pfb[2 * C::MT];        // BF16 P(t-1) operand, one per 16-key k-step
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) psc[nb] = 127;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-
-    if (kt < w_kt) {
-      const char* ks_ = lds + buf * C::STAGE;
-      const char* vs_ = ks_ + C::K_BYTES;
-
-      // S^T = K Q^T : MT 32-key M-tiles
-      f32x16 s[C::MT];
+  auto mfma_phase = [&](int t) {
+    const int st_cur = t % C::NSTAGE;
+    const int st_prev = (t + C::NSTAGE - 1) % C::NSTAGE;
+    const int st_next = (t + 1) % C::NSTAGE;
+    __builtin_amdgcn_s_setprio(1);
+    // stage tile t+1 (its loads were issued one matrix phase ago), then load tile t+2
+    if (t + 1 < n_kt) store_tile(st_next);
+    if (t + 2 < n_kt) load_tile(t + 2);
+    // O^T += V^T P^T of tile t-1
+    if (t >= 1 && t - 1 < w_kt) {
+      const char* vs_ = lds + st_prev * C::STAGE + C::K_BYTES;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+          for (int md = 0; md < DV / 32; ++md) {
+            const int row = 32 * md + l32;
+            const char* rp = vs_ + row * C::VROW;
+            const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g));
+            const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g + 16));
+            i32x8 vf;
+            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
+            vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+            oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                vf, pf8[nb], oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc[nb]);
+          }
+          if constexpr (!WANT_LSE) {
+            // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
+            i32x8 ones;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
+            f32x16 z;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[i] = 0.f;
+            z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf8[nb], z, 0, 0, 0,
+                                                                0x7f7f7f7f, 0, psc[nb]);
+            l_run += z[0];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 2 * C::MT; ++kk) {
+#pragma unroll
+          for (int md = 0; md < DV / 32; ++md) {
+            const int row = 32 * md + l32;
+            const uint4 a = *(const uint4*)(vs_ + row * C::VROW +
+                                            vswz<C::VCH>(row, 2 * (16 * kk + 8 * g)));
+            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a, pfb[kk],
+                                                               oacc[md], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // S^T = K Q^T of tile t
+    if (t < w_kt) {
+      const char* ks_ = lds + st_cur * C::STAGE;
 #pragma unroll
       for (int m = 0; m < C::MT; ++m)
 #pragma unroll
@@ -395,142 +457,127 @@ void attn_fwd_kernel(FwdParams p) {
           }
         }
       }
+    }
+  };
 
-      // causal mask on the tile(s) that cross this wave's diagonal
-      if (kt * BN + BN - 1 > q0w) {
-        const int qrow = q0w + l32;
+  auto valu_phase = [&](int t) {
+    __builtin_amdgcn_s_setprio(0);
+    if (t >= w_kt) return;
+    // causal mask on the tile(s) that cross this wave's diagonal
+    if (t * BN + BN - 1 > q0w) {
+      // element i of M-tile m holds key t*BN + 32m + 4g + off_i, off_i = 8(i/4) + i%4;
+      // it is masked when off_i > d_m = qrow - (t*BN + 32m + 4g).  Select with integer
+      // ops (sign of d_m - off_i) rather than per-element lane-mask compares.
+      const int d0 = q0w + l32 - (t * BN + 4 * g);
 #pragma unroll
-        for (int m = 0; m < C::MT; ++m)
+      for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt * BN + 32 * m + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow) s[m][i] = -INFINITY;
-          }
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int keep = (d0 - 32 * m - (8 * (i >> 2) + (i & 3))) >> 31;   // -1: masked
+          const uint32_t bits = __float_as_uint(s[m][i]);
+          s[m][i] = __uint_as_float((bits & ~(uint32_t)keep) | (0xff800000u & (uint32_t)keep));
+        }
+    }
+    // max over each 64-key block (this lane's 32 keys, then the other lane half's)
+    float bmx[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      bmx[nb] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) bmx[nb] = fmaxf(bmx[nb], s[2 * nb + (e >> 4)][e & 15]);
+      if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
+    }
+    float mx = bmx[0];
+#pragma unroll
+    for (int nb = 1; nb < C::NB; ++nb) mx = fmaxf(mx, bmx[nb]);
+    // lazy running max: rescale only when some row's tile max exceeds m by > TAU
+    if (__any((mx - m_run) * c > TAU)) {
+      const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+      if (WANT_LSE) lx_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+    }
+    const float nmc = -m_run * c;
 
-      // max over each 64-key block (this lane's 32 keys, then the other lane half's)
-      float bmx[C::NB];
+    if constexpr (FP8) {
+      const float A = 8.f * c;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        bmx[nb] = -INFINITY;
+        // one block exponent per query and 64-key block (both operand scale blocks)
+        const float xmax = fmaf(bmx[nb], c, nmc);
+        const float kbf = fminf(floorf(8.f - xmax), 127.f);
+        psc[nb] = 127 - (int)kbf;
+        if constexpr (WANT_LSE) {
+          // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
+          // fp32 sum (scale removed) normalises O and gives the log-sum-exp
+          const float off = nmc + kbf;
+          float bs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) bmx[nb] = fmaxf(bmx[nb], s[2 * nb + (e >> 4)][e & 15]);
-        if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
-      }
-      float mx = bmx[0];
+          for (int w = 0; w < 8; ++w) {
+            float pv[4];
 #pragma unroll
-      for (int nb = 1; nb < C::NB; ++nb) mx = fmaxf(mx, bmx[nb]);
-      // lazy running max: rescale only when some row's tile max exceeds m by > TAU
-      if (__any((mx - m_run) * c > TAU)) {
-        const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        l_run *= alpha;
-        if (WANT_LSE) lx_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < DV / 32; ++md)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
-      }
-      const float nmc = -m_run * c;
-
-      if constexpr (FP8) {
-        const float A = 8.f * c;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          // one block exponent per query and 64-key block (both operand scale blocks)
-          const float xmax = fmaf(bmx[nb], c, nmc);
-          const float kbf = fminf(floorf(8.f - xmax), 127.f);
-          const int psc = 127 - (int)kbf;
-          i32x8 pf;
-          if constexpr (WANT_LSE) {
-            // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
-            // fp32 sum (scale removed) normalises O and gives the log-sum-exp
-            const float off = nmc + kbf;
-            float bs = 0.f;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-              float pv[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int e = 4 * w + j;
-                pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
-                bs += pv[j];
-              }
-              int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-              word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
-              pf[w] = word;
+            for (int j = 0; j < 4; ++j) {
+              const int e = 4 * w + j;
+              pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
+              bs += pv[j];
             }
-            lx_run += __builtin_ldexpf(bs, -(int)kbf);
-          } else {
-            // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
-            const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+            pf8[nb][w] = word;
+          }
+          lx_run += __builtin_ldexpf(bs, -(int)kbf);
+        } else {
+          // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
+          const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-              uint32_t word = 0u;
+          for (int w = 0; w < 8; ++w) {
+            uint32_t word = 0u;
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int e = 4 * w + j;
-                word = __builtin_amdgcn_cvt_pk_u8_f32(
-                    fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc), j, word);
-              }
-              pf[w] = (int)word;
+            for (int j = 0; j < 4; ++j) {
+              const int e = 4 * w + j;
+              word = __builtin_amdgcn_cvt_pk_u8_f32(
+                  fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc), j, word);
             }
-          }
-          // O^T += V^T P^T, block scale removed by the scaled MFMA
-#pragma unroll
-          for (int md = 0; md < DV / 32; ++md) {
-            const int row = 32 * md + l32;
-            const char* rp = vs_ + row * C::VROW;
-            const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g));
-            const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g + 16));
-            i32x8 vf;
-            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
-            vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
-            oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                vf, pf, oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc);
-          }
-          if constexpr (!WANT_LSE) {
-            // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
-            i32x8 ones;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
-            f32x16 z;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) z[i] = 0.f;
-            z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, z, 0, 0, 0,
-                                                                0x7f7f7f7f, 0, psc);
-            l_run += z[0];
-          }
-        }
-      } else {
-        bf16x8 pf[C::MT * 2];
-        float rs = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16 * C::MT; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c, nmc));
-          rs += pv;
-          pf[e >> 3][e & 7] = (__bf16)pv;
-        }
-        l_run += rs;
-        // O^T += V^T P^T over k-steps of 16 keys
-#pragma unroll
-        for (int kk = 0; kk < 2 * C::MT; ++kk) {
-#pragma unroll
-          for (int md = 0; md < DV / 32; ++md) {
-            const int row = 32 * md + l32;
-            const uint4 a = *(const uint4*)(vs_ + row * C::VROW +
-                                            vswz<C::VCH>(row, 2 * (16 * kk + 8 * g)));
-            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a, pf[kk],
-                                                               oacc[md], 0, 0, 0);
+            pf8[nb][w] = (int)word;
           }
         }
       }
+    } else {
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16 * C::MT; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c, nmc));
+        rs += pv;
+        pfb[e >> 3][e & 7] = (__bf16)pv;
+      }
+      l_run += rs;
     }
+  };
 
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+  load_tile(0);
+  store_tile(0);
+  // All prologue loads (Q fragments, tile 0) have landed: say so explicitly, so the
+  // loop does not wait on later tiles' loads before its first matrix instruction.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  if (n_kt > 1) load_tile(1);
+  __syncthreads();
+  if (grp_b) __syncthreads();           // group B runs half a phase behind group A
+
+  for (int t = 0; t <= n_kt; ++t) {
+    mfma_phase(t);
     __syncthreads();
+    if (t < n_kt) {
+      valu_phase(t);
+      __syncthreads();
+    }
   }
+  if (!grp_b) __syncthreads();          // equal barrier counts in both groups
+  __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------
   const int qrow = q0w + l32;
@@ -574,10 +621,10 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream) {
   if (fp8) {
-    if (d_qk == 128) return launch_cfg<true, 128, 128, 4>(p, stream);
-    return launch_cfg<true, 192, 64, 4>(p, stream);
+    if (d_qk == 128) return launch_cfg<true, 128, 128, 8>(p, stream);
+    return launch_cfg<true, 192, 64, 8>(p, stream);
   }
-  if (d_qk == 128) return launch_cfg<false, 128, 64, 4>(p, stream);
+  if (d_qk == 128) return launch_cfg<false, 128, 64, 8>(p, stream);
   return launch_cfg<false, 192, 64, 8>(p, stream);
 }
 

@@ -83,7 +83,8 @@ struct Cfg {
   static constexpr int VROW = BN * EB + 16;          // padded LDS row of V^T
   static constexpr int VCH = BN * EB / 16;           // 16-byte chunks per V^T row
   static constexpr int VK = FP8 ? 8 : 4;             // keys per V copy unit
-  static constexpr int VUN = (BN / VK) * (DV / 8);   // units of VK keys x 8 channels
+  static constexpr int VC = 4;                       // channels per V copy unit
+  static constexpr int VUN = (BN / VK) * (DV / VC);  // units of VK keys x VC channels
   static constexpr int VPT = (VUN + NT - 1) / NT;
   static constexpr int K_BYTES = BN * KROW;
   static constexpr int V_BYTES = DV * VROW;
@@ -162,6 +163,13 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// An empty instruction that reads x: the value must be computed by this point.
+__device__ __forceinline__ void keep_in_vgprs(const f32x16& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
 __device__ __forceinline__ i32x8 load_i32x8(const char* p) {
   const uint4 a = *(const uint4*)p;
   const uint4 b = *(const uint4*)(p + 16);
@@ -230,7 +238,7 @@ void attn_fwd_kernel(FwdParams p) {
   // Buffer loads: each thread copies the same byte offsets of every tile; keys past N
   // in the last tile read as zeros (they are masked: key > every query row).
   uint4 kreg[C::KPT];
-  typedef typename std::conditional<FP8, uint2, uint4>::type VLoad;
+  typedef typename std::conditional<FP8, uint32_t, uint2>::type VLoad;   // VC channels
   VLoad vreg[C::VPT][C::VK];
   uint32_t koff[C::KPT], voff[C::VPT][C::VK];
 #pragma unroll
@@ -242,11 +250,11 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int u = 0; u < C::VPT; ++u) {
     const int uu = tid + u * C::NT;
-    const int dc = uu & 15, ku = uu >> 4;
+    const int dc = uu % (DV / C::VC), ku = uu / (DV / C::VC);
 #pragma unroll
     for (int j = 0; j < C::VK; ++j)
       voff[u][j] = (uint32_t)vunit_key<FP8>(ku, j) * (uint32_t)vstride +
-                   (uint32_t)(dc * 8 * C::EB);
+                   (uint32_t)(dc * C::VC * C::EB);
   }
 
   // One descriptor per tensor for the whole key range of this (b, kv head); a tile is
@@ -272,10 +280,9 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < C::VK; ++j) {
         if constexpr (FP8) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff[u][j] + vt_off, 0, 0);
-          vreg[u][j] = *(const VLoad*)&x;
+          vreg[u][j] = __builtin_amdgcn_raw_buffer_load_b32(vrsrc, voff[u][j] + vt_off, 0, 0);
         } else {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff[u][j] + vt_off, 0, 0);
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff[u][j] + vt_off, 0, 0);
           vreg[u][j] = *(const VLoad*)&x;
         }
       }
@@ -296,52 +303,44 @@ void attn_fwd_kernel(FwdParams p) {
     for (int u = 0; u < C::VPT; ++u) {
       const int uu = tid + u * C::NT;
       if (C::VUN % C::NT != 0 && uu >= C::VUN) break;
-      const int dc = uu & 15, ku = uu >> 4;
+      const int dc = uu % (DV / C::VC), ku = uu / (DV / C::VC);
       const int pos = vunit_pos<FP8>(ku);
       if constexpr (FP8) {
-        // 8 keys x 8 channels of bytes -> 8 rows (channels) of 8 key bytes.
-        uint32_t wd[2][8];
+        // 8 keys x 4 channels of bytes -> 4 rows (channels) of 8 key bytes.
+        uint32_t wd[2][4];
 #pragma unroll
         for (int h4 = 0; h4 < 2; ++h4) {
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const uint32_t a0 = w ? vreg[u][4 * h4 + 0].y : vreg[u][4 * h4 + 0].x;
-            const uint32_t a1 = w ? vreg[u][4 * h4 + 1].y : vreg[u][4 * h4 + 1].x;
-            const uint32_t a2 = w ? vreg[u][4 * h4 + 2].y : vreg[u][4 * h4 + 2].x;
-            const uint32_t a3 = w ? vreg[u][4 * h4 + 3].y : vreg[u][4 * h4 + 3].x;
-            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-            wd[h4][4 * w + 0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-            wd[h4][4 * w + 1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-            wd[h4][4 * w + 2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-            wd[h4][4 * w + 3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-          }
+          const uint32_t a0 = vreg[u][4 * h4 + 0], a1 = vreg[u][4 * h4 + 1];
+          const uint32_t a2 = vreg[u][4 * h4 + 2], a3 = vreg[u][4 * h4 + 3];
+          const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+          const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+          const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+          const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+          wd[h4][0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+          wd[h4][1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+          wd[h4][2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+          wd[h4][3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int row = dc * 8 + r;
+        for (int r = 0; r < C::VC; ++r) {
+          const int row = dc * C::VC + r;
           *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, pos)) =
               make_uint2(wd[0][r], wd[1][r]);
         }
       } else {
-        // 4 keys x 8 channels of bf16 -> 8 rows (channels) of 4 keys (8 bytes).
-        const uint32_t* r0 = (const uint32_t*)&vreg[u][0];
-        const uint32_t* r1 = (const uint32_t*)&vreg[u][1];
-        const uint32_t* r2 = (const uint32_t*)&vreg[u][2];
-        const uint32_t* r3 = (const uint32_t*)&vreg[u][3];
+        // 4 keys x 4 channels of bf16 -> 4 rows (channels) of 4 keys (8 bytes).
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
-            uint2 val;
-            val.x = __builtin_amdgcn_perm(r1[w], r0[w], sel);
-            val.y = __builtin_amdgcn_perm(r3[w], r2[w], sel);
-            const int row = dc * 8 + 2 * w + hh;
-            *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, 2 * pos)) = val;
-          }
+        for (int r = 0; r < C::VC; ++r) {
+          const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w0 = (r & 2) ? vreg[u][0].y : vreg[u][0].x;
+          const uint32_t w1 = (r & 2) ? vreg[u][1].y : vreg[u][1].x;
+          const uint32_t w2 = (r & 2) ? vreg[u][2].y : vreg[u][2].x;
+          const uint32_t w3 = (r & 2) ? vreg[u][3].y : vreg[u][3].x;
+          uint2 val;
+          val.x = __builtin_amdgcn_perm(w1, w0, sel);
+          val.y = __builtin_amdgcn_perm(w3, w2, sel);
+          const int row = dc * C::VC + r;
+          *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, 2 * pos)) = val;
         }
       }
     }
@@ -377,8 +376,106 @@ void attn_fwd_kernel(FwdParams p) {
   i32x8 pf8[C::NB];             // FP8 P(t-1) operand, one per 64-key block
   int psc[C::NB];               // its E8M0 block scales
   bf16x8 pfb[2 * C::MT];        // BF16 P(t-1) operand, one per 16-key k-step
+
+  // Matrix-phase slots: the P V MFMAs of tile t-1 (NPV of them) followed by the Q K^T
+  // MFMAs of tile t (NQK).  The LDS operand of slot j+LA is requested while slot j's
+  // MFMA runs, so the matrix pipe does not wait on LDS latency between MFMAs.
+  constexpr int NMD = DV / 32;
+  constexpr int NPV = FP8 ? C::NB * NMD : 2 * C::MT * NMD;
+  constexpr int NQK = C::KS * C::MT;
+  constexpr int LA = FP8 ? 2 : 3;
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type Frag;
+  f32x16 zero16;
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) psc[nb] = 127;
+  for (int i = 0; i < 16; ++i) zero16[i] = 0.f;
+
+  auto load_frag = [&](int j, const char* ks_, const char* vs_) -> Frag {
+    if (j < NPV) {                       // V^T rows 32md.., keys of block nb / step kk
+      const int md = j % NMD, row = 32 * md + l32;
+      const char* rp = vs_ + row * C::VROW;
+      if constexpr (FP8) {
+        const int x = 64 * (j / NMD) + 32 * g;
+        const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, x));
+        const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, x + 16));
+        i32x8 f;
+        f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
+        f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+        return f;
+      } else {
+        const uint4 a = *(const uint4*)(rp + vswz<C::VCH>(row, 2 * (16 * (j / NMD) + 8 * g)));
+        return *(const Frag*)&a;
+      }
+    } else {                             // K rows 32m.., channels of k-step ks
+      const int jj = j - NPV, ks = jj / C::MT, m = jj % C::MT;
+      const char* rp = ks_ + (32 * m + l32) * C::KROW;
+      if constexpr (FP8) {
+        return load_i32x8(rp + 64 * ks + 32 * g);
+      } else {
+        const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
+        return *(const Frag*)&a;
+      }
+    }
+  };
+
+  f32x16 zrow;   // FP8 Lean P: rounded-code row sums of tile t-1 (element 0)
+  auto do_mfma = [&](int j, const Frag& f) {
+    if (j < NPV) {
+      const int md = j % NMD, blk = j / NMD;
+      if constexpr (FP8) {
+        oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f, pf8[blk], oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
+        if (!WANT_LSE && md == NMD - 1) {
+          // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
+          i32x8 ones;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
+          if (blk == 0)
+            zrow = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ones, pf8[blk], zero16, 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
+          else
+            zrow = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ones, pf8[blk], zrow, 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
+        }
+      } else {
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pfb[blk], oacc[md], 0, 0, 0);
+      }
+    } else {
+      const int jj = j - NPV, ks = jj / C::MT, m = jj % C::MT;
+      if (ks == 0) {
+        if constexpr (FP8) {
+          s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f, *(const i32x8*)&qf[ks], zero16, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+        } else {
+          s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, *(const bf16x8*)&qf[ks], zero16,
+                                                         0, 0, 0);
+        }
+      } else {
+        if constexpr (FP8) {
+          s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f, *(const i32x8*)&qf[ks], s[m], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+        } else {
+          s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, *(const bf16x8*)&qf[ks], s[m],
+                                                         0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // slots [J0, J1) with an LA-deep operand pipeline
+  auto run_slots = [&]<int J0, int J1>(const char* ks_, const char* vs_) {
+    Frag fr[LA + 1];
+#pragma unroll
+    for (int j = J0; j < J0 + LA && j < J1; ++j) fr[(j - J0) % (LA + 1)] = load_frag(j, ks_, vs_);
+#pragma unroll
+    for (int j = J0; j < J1; ++j) {
+      // keep the slots in program order: the scheduler would otherwise hoist every
+      // operand read to the top of the phase and run out of registers
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + LA < J1) fr[(j + LA - J0) % (LA + 1)] = load_frag(j + LA, ks_, vs_);
+      do_mfma(j, fr[(j - J0) % (LA + 1)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   auto mfma_phase = [&](int t) {
     const int st_cur = t % C::NSTAGE;
@@ -388,81 +485,39 @@ void attn_fwd_kernel(FwdParams p) {
     // stage tile t+1 (its loads were issued one matrix phase ago), then load tile t+2
     if (t + 1 < n_kt) store_tile(st_next);
     if (t + 2 < n_kt) load_tile(t + 2);
-    // O^T += V^T P^T of tile t-1
-    if (t >= 1 && t - 1 < w_kt) {
-      const char* vs_ = lds + st_prev * C::STAGE + C::K_BYTES;
-      if constexpr (FP8) {
+    // Every matrix phase runs all slots, so the phase is one straight-line schedule.
+    // Where a wave has no work the slots are made harmless instead of skipped: the P
+    // operand is zero (set by the softmax phase, or initially) and, at t = 0, V is read
+    // from the valid tile-0 stage; a Q K^T past the wave's last tile is never used.
+    const char* ks_ = lds + st_cur * C::STAGE;
+    const char* vs_ = lds + (t == 0 ? st_cur : st_prev) * C::STAGE + C::K_BYTES;
+    run_slots.template operator()<0, NPV + NQK>(ks_, vs_);
+    if (FP8 && !WANT_LSE) l_run += zrow[0];
+    // Pin the scores to this phase: their only readers are in the softmax phase's
+    // branch, and the compiler would otherwise sink the Q K^T MFMAs past the barrier.
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
+    for (int m = 0; m < C::MT; ++m) keep_in_vgprs(s[m]);
+  };
+
+  auto zero_p = [&]() {
 #pragma unroll
-          for (int md = 0; md < DV / 32; ++md) {
-            const int row = 32 * md + l32;
-            const char* rp = vs_ + row * C::VROW;
-            const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g));
-            const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, 64 * nb + 32 * g + 16));
-            i32x8 vf;
-            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
-            vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
-            oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                vf, pf8[nb], oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc[nb]);
-          }
-          if constexpr (!WANT_LSE) {
-            // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
-            i32x8 ones;
+    for (int nb = 0; nb < C::NB; ++nb) {
+      psc[nb] = 127;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
-            f32x16 z;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) z[i] = 0.f;
-            z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf8[nb], z, 0, 0, 0,
-                                                                0x7f7f7f7f, 0, psc[nb]);
-            l_run += z[0];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 2 * C::MT; ++kk) {
-#pragma unroll
-          for (int md = 0; md < DV / 32; ++md) {
-            const int row = 32 * md + l32;
-            const uint4 a = *(const uint4*)(vs_ + row * C::VROW +
-                                            vswz<C::VCH>(row, 2 * (16 * kk + 8 * g)));
-            oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a, pfb[kk],
-                                                               oacc[md], 0, 0, 0);
-          }
-        }
-      }
+      for (int w = 0; w < 8; ++w) pf8[nb][w] = 0;
     }
-    // S^T = K Q^T of tile t
-    if (t < w_kt) {
-      const char* ks_ = lds + st_cur * C::STAGE;
 #pragma unroll
-      for (int m = 0; m < C::MT; ++m)
+    for (int kk = 0; kk < 2 * C::MT; ++kk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[m][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int m = 0; m < C::MT; ++m) {
-          const char* rp = ks_ + (32 * m + l32) * C::KROW;
-          if constexpr (FP8) {
-            const i32x8 kf = load_i32x8(rp + 64 * ks + 32 * g);
-            s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                kf, *(const i32x8*)&qf[ks], s[m], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
-          } else {
-            const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
-            s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&a,
-                                                           *(const bf16x8*)&qf[ks], s[m],
-                                                           0, 0, 0);
-          }
-        }
-      }
-    }
+      for (int e = 0; e < 8; ++e) pfb[kk][e] = (__bf16)0.f;
   };
 
   auto valu_phase = [&](int t) {
     __builtin_amdgcn_s_setprio(0);
-    if (t >= w_kt) return;
+    if (t >= w_kt) {        // past this wave's last tile: the next P V adds nothing
+      zero_p();
+      return;
+    }
     // causal mask on the tile(s) that cross this wave's diagonal
     if (t * BN + BN - 1 > q0w) {
       // element i of M-tile m holds key t*BN + 32m + 4g + off_i, off_i = 8(i/4) + i%4;
@@ -482,9 +537,10 @@ void attn_fwd_kernel(FwdParams p) {
     float bmx[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
-      bmx[nb] = -INFINITY;
+      float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
 #pragma unroll
-      for (int e = 0; e < 32; ++e) bmx[nb] = fmaxf(bmx[nb], s[2 * nb + (e >> 4)][e & 15]);
+      for (int e = 0; e < 32; ++e) pm[e & 3] = fmaxf(pm[e & 3], s[2 * nb + (e >> 4)][e & 15]);
+      bmx[nb] = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
       if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
     }
     float mx = bmx[0];
@@ -516,7 +572,7 @@ void attn_fwd_kernel(FwdParams p) {
           // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
           // fp32 sum (scale removed) normalises O and gives the log-sum-exp
           const float off = nmc + kbf;
-          float bs = 0.f;
+          float bs[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             float pv[4];
@@ -524,13 +580,13 @@ void attn_fwd_kernel(FwdParams p) {
             for (int j = 0; j < 4; ++j) {
               const int e = 4 * w + j;
               pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
-              bs += pv[j];
+              bs[j] += pv[j];
             }
             int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
             word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
             pf8[nb][w] = word;
           }
-          lx_run += __builtin_ldexpf(bs, -(int)kbf);
+          lx_run += __builtin_ldexpf((bs[0] + bs[1]) + (bs[2] + bs[3]), -(int)kbf);
         } else {
           // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
           const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
@@ -548,35 +604,44 @@ void attn_fwd_kernel(FwdParams p) {
         }
       }
     } else {
-      float rs = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};     // independent partial sums
 #pragma unroll
       for (int e = 0; e < 16 * C::MT; ++e) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c, nmc));
-        rs += pv;
+        rs[e & 3] += pv;
         pfb[e >> 3][e & 7] = (__bf16)pv;
       }
-      l_run += rs;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
   };
 
+  // Workgroup barrier that the compiler may not schedule anything across (matrix
+  // instructions touch no memory, so it would otherwise move them over barriers).
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  zero_p();                             // the first matrix phase has no P yet
   load_tile(0);
   store_tile(0);
   // All prologue loads (Q fragments, tile 0) have landed: say so explicitly, so the
   // loop does not wait on later tiles' loads before its first matrix instruction.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (n_kt > 1) load_tile(1);
-  __syncthreads();
-  if (grp_b) __syncthreads();           // group B runs half a phase behind group A
+  phase_barrier();
+  if (grp_b) phase_barrier();           // group B runs half a phase behind group A
 
   for (int t = 0; t <= n_kt; ++t) {
     mfma_phase(t);
-    __syncthreads();
+    phase_barrier();
     if (t < n_kt) {
       valu_phase(t);
-      __syncthreads();
+      phase_barrier();
     }
   }
-  if (!grp_b) __syncthreads();          // equal barrier counts in both groups
+  if (!grp_b) phase_barrier();          // equal barrier counts in both groups
   __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------

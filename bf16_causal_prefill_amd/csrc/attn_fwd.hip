@@ -21,11 +21,12 @@
 // transposed, O^T = V^T P^T: the B operand P^T needs, per lane, probabilities of its own
 // query, which are exactly the values the lane already holds, so P goes from the score
 // accumulator to the MFMA operand without any cross-lane movement.  The keys a lane
-// holds are not contiguous (rows 8*(i/4) + 4*(lane/32) + i%4 of the accumulator), so V
-// is written to LDS transposed (V^T, one row per head-dim channel) with the keys of each
-// row permuted so that the 8 (bf16) or 32 (fp8) keys a lane needs for one MFMA are
-// contiguous: the contraction over keys does not care about key order as long as both
-// operands use the same one.
+// holds are not contiguous (rows 8*(i/4) + 4*(lane/32) + i%4 of the accumulator); the
+// contraction over keys does not care about key order as long as both operands use the
+// same one, so the V^T operand is gathered in exactly that key order.  V stays in LDS
+// as it is stored in memory (one row of channels per key) and gfx950's transposing LDS
+// reads (ds_read_b64_tr_b8 / _b16) turn 8 key rows x 8 bytes into one channel's 8 keys
+// per lane, with each lane of a 16-lane group addressing the key row it contributes.
 //
 // Lazy rescaling.  The running max m of a query only moves when a tile's max exceeds it
 // by more than TAU (log2 units); otherwise the tile's probabilities are taken relative to
@@ -58,6 +59,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int DV = 128;    // value head dim (both supported shapes)
 constexpr float LOG2E = 1.4426950408889634f;
@@ -80,14 +83,12 @@ struct Cfg {
   static constexpr int R16 = KRB / 16;               // 16-byte chunks per K row
   static constexpr int KCH = BN * R16;               // chunks per K tile
   static constexpr int KPT = (KCH + NT - 1) / NT;    // K chunks per thread
-  static constexpr int VROW = BN * EB + 16;          // padded LDS row of V^T
-  static constexpr int VCH = BN * EB / 16;           // 16-byte chunks per V^T row
-  static constexpr int VK = FP8 ? 8 : 4;             // keys per V copy unit
-  static constexpr int VC = 4;                       // channels per V copy unit
-  static constexpr int VUN = (BN / VK) * (DV / VC);  // units of VK keys x VC channels
-  static constexpr int VPT = (VUN + NT - 1) / NT;
+  static constexpr int VROW = DV * EB;               // LDS row of the V tile (one key)
+  static constexpr int VCPR = VROW / 16;             // 16-byte chunks per V row
+  static constexpr int VCH = BN * VCPR;              // chunks per V tile
+  static constexpr int VPT = (VCH + NT - 1) / NT;    // V chunks per thread
   static constexpr int K_BYTES = BN * KROW;
-  static constexpr int V_BYTES = DV * VROW;
+  static constexpr int V_BYTES = BN * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int NSTAGE = 3;                   // K/V tiles resident at once
   static constexpr int LDS = NSTAGE * STAGE;
@@ -98,34 +99,14 @@ struct Cfg {
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
 };
 
-// V^T key order.  Inside a row of the LDS V^T tile the keys are permuted so that the
-// keys one lane feeds to one P V MFMA are contiguous (see the file comment):
-//   FP8:  key 64n + 32m + 8a + 4g + b  sits at  64n + 32g + 16m + 4a + b
-//   BF16: key 16s + 8a + 4g + b        sits at  16s + 8g + 4a + b
-// A copy unit is a set of keys whose positions are contiguous: FP8 units hold 8 keys
-// (kbase + {0..3, 8..11}, 8 positions), BF16 units 4 keys (4 positions).
+// The 16-byte chunks of key row k of the LDS V tile are XOR-permuted by vswz<FP8>(k).
+// A transposing operand read makes each 16-lane group fetch 16 bytes from each of 8
+// (fp8) or 4 (bf16) key rows that share their chunk index, and two groups (the two
+// 16-channel halves of a 32-channel block) are served per LDS cycle; this permutation
+// puts those 16 row segments in 16 different 4-bank groups.
 template <bool FP8>
-__device__ __forceinline__ int vunit_key0(int ku) {
-  if (FP8) return 64 * (ku >> 3) + 32 * ((ku >> 2) & 1) + 16 * ((ku >> 1) & 1) + 4 * (ku & 1);
-  return 4 * ku;
-}
-template <bool FP8>
-__device__ __forceinline__ int vunit_key(int ku, int j) {   // j-th key of unit ku
-  if (FP8) return vunit_key0<true>(ku) + (j & 3) + 8 * (j >> 2);
-  return 4 * ku + j;
-}
-template <bool FP8>
-__device__ __forceinline__ int vunit_pos(int ku) {          // first position of unit ku
-  if (FP8) return 64 * (ku >> 3) + 32 * (ku & 1) + 16 * ((ku >> 2) & 1) + 8 * ((ku >> 1) & 1);
-  return 16 * (ku >> 2) + 8 * (ku & 1) + 4 * ((ku >> 1) & 1);
-}
-
-// Byte offset of logical byte x of V^T row `row`: the row's 16-byte chunks are
-// XOR-swizzled by (row / 16), so the 16 lanes that store the same positions of 16
-// different 8-channel groups hit different LDS banks.
-template <int VCH>
-__device__ __forceinline__ int vswz(int row, int x) {
-  return (((x >> 4) ^ ((row >> 4) & (VCH - 1))) << 4) | (x & 15);
+__device__ __forceinline__ int vswz(int key) {
+  return FP8 ? 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1) : 4 * (key & 3);
 }
 
 // Maps the flat workgroup id to (batch, query head, query tile).  Heaviest causal
@@ -238,9 +219,8 @@ void attn_fwd_kernel(FwdParams p) {
   // Buffer loads: each thread copies the same byte offsets of every tile; keys past N
   // in the last tile read as zeros (they are masked: key > every query row).
   uint4 kreg[C::KPT];
-  typedef typename std::conditional<FP8, uint32_t, uint2>::type VLoad;   // VC channels
-  VLoad vreg[C::VPT][C::VK];
-  uint32_t koff[C::KPT], voff[C::VPT][C::VK];
+  uint4 vreg[C::VPT];
+  uint32_t koff[C::KPT], voff[C::VPT];
 #pragma unroll
   for (int cix = 0; cix < C::KPT; ++cix) {
     const int cc = tid + cix * C::NT;
@@ -249,12 +229,9 @@ void attn_fwd_kernel(FwdParams p) {
   }
 #pragma unroll
   for (int u = 0; u < C::VPT; ++u) {
-    const int uu = tid + u * C::NT;
-    const int dc = uu % (DV / C::VC), ku = uu / (DV / C::VC);
-#pragma unroll
-    for (int j = 0; j < C::VK; ++j)
-      voff[u][j] = (uint32_t)vunit_key<FP8>(ku, j) * (uint32_t)vstride +
-                   (uint32_t)(dc * C::VC * C::EB);
+    const int cc = tid + u * C::NT;
+    const int row = cc / C::VCPR, col = cc - row * C::VCPR;
+    voff[u] = (uint32_t)row * (uint32_t)vstride + (uint32_t)col * 16u;
   }
 
   // One descriptor per tensor for the whole key range of this (b, kv head); a tile is
@@ -276,16 +253,9 @@ void attn_fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
-      if (C::VUN % C::NT != 0 && tid + u * C::NT >= C::VUN) break;
-#pragma unroll
-      for (int j = 0; j < C::VK; ++j) {
-        if constexpr (FP8) {
-          vreg[u][j] = __builtin_amdgcn_raw_buffer_load_b32(vrsrc, voff[u][j] + vt_off, 0, 0);
-        } else {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff[u][j] + vt_off, 0, 0);
-          vreg[u][j] = *(const VLoad*)&x;
-        }
-      }
+      if (C::VCH % C::NT != 0 && tid + u * C::NT >= C::VCH) break;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff[u] + vt_off, 0, 0);
+      vreg[u] = *(const uint4*)&x;
     }
   };
 
@@ -301,48 +271,10 @@ void attn_fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
-      const int uu = tid + u * C::NT;
-      if (C::VUN % C::NT != 0 && uu >= C::VUN) break;
-      const int dc = uu % (DV / C::VC), ku = uu / (DV / C::VC);
-      const int pos = vunit_pos<FP8>(ku);
-      if constexpr (FP8) {
-        // 8 keys x 4 channels of bytes -> 4 rows (channels) of 8 key bytes.
-        uint32_t wd[2][4];
-#pragma unroll
-        for (int h4 = 0; h4 < 2; ++h4) {
-          const uint32_t a0 = vreg[u][4 * h4 + 0], a1 = vreg[u][4 * h4 + 1];
-          const uint32_t a2 = vreg[u][4 * h4 + 2], a3 = vreg[u][4 * h4 + 3];
-          const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-          const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-          const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-          const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-          wd[h4][0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-          wd[h4][1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-          wd[h4][2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-          wd[h4][3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-        }
-#pragma unroll
-        for (int r = 0; r < C::VC; ++r) {
-          const int row = dc * C::VC + r;
-          *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, pos)) =
-              make_uint2(wd[0][r], wd[1][r]);
-        }
-      } else {
-        // 4 keys x 4 channels of bf16 -> 4 rows (channels) of 4 keys (8 bytes).
-#pragma unroll
-        for (int r = 0; r < C::VC; ++r) {
-          const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t w0 = (r & 2) ? vreg[u][0].y : vreg[u][0].x;
-          const uint32_t w1 = (r & 2) ? vreg[u][1].y : vreg[u][1].x;
-          const uint32_t w2 = (r & 2) ? vreg[u][2].y : vreg[u][2].x;
-          const uint32_t w3 = (r & 2) ? vreg[u][3].y : vreg[u][3].x;
-          uint2 val;
-          val.x = __builtin_amdgcn_perm(w1, w0, sel);
-          val.y = __builtin_amdgcn_perm(w3, w2, sel);
-          const int row = dc * C::VC + r;
-          *(uint2*)(vs_ + row * C::VROW + vswz<C::VCH>(row, 2 * pos)) = val;
-        }
-      }
+      const int cc = tid + u * C::NT;
+      if (C::VCH % C::NT != 0 && cc >= C::VCH) break;
+      const int row = cc / C::VCPR, col = cc - row * C::VCPR;
+      *(uint4*)(vs_ + row * C::VROW + 16 * (col ^ vswz<FP8>(row))) = vreg[u];
     }
   };
 
@@ -389,21 +321,62 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero16[i] = 0.f;
 
+  // Transposing V reads.  A P V MFMA needs, in lane l, channel 32md + l%32 of the keys
+  // whose probabilities lane l holds, in the order it holds them:
+  //   FP8, 64-key block n, operand byte j (k-index 32g + j):
+  //     key 64n + 32(j/16) + 8((j%16)/4) + 4g + j%4
+  //   BF16, 16-key step kk, operand element i (k-index 8g + i):
+  //     key 32(kk/2) + 16(kk%2) + 8(i/4) + 4g + i%4
+  // ds_read_b64_tr_b8 gives lane L of a 16-lane group byte (L%8) of the 8-byte chunks
+  // addressed by group lanes 2j + L/8 (j = 0..7); ds_read_b64_tr_b16 gives it halfword
+  // (L%4) of the chunks addressed by group lanes 4j + L/4 (j = 0..3).  So group lane s
+  // addresses, for FP8 read r (operand bytes 8r..8r+7), key row 16r + 8(s/8) + 4g +
+  // (s/2)%4 at channels 16(s/16 of the 32-lane half) + 8(s%2); for BF16 read r (elements
+  // 4r..4r+3), key row 8r + 4g + s/4 at channels 4(s%4).  The lane-dependent part of
+  // that address (and the channel block md) is precomputed; block, step and read
+  // indices add compile-time row offsets, which leave vswz unchanged (it only looks at
+  // key bits the lane fixes).
+  int vrd[NMD];
+  {
+    const int s16 = lane & 15, grp = (lane >> 4) & 1;
+    if constexpr (FP8) {
+      const int kl = 8 * (s16 >> 3) + 4 * g + ((s16 >> 1) & 3);
+      const int f = vswz<true>(kl);
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+        vrd[md] = kl * C::VROW + 16 * (((2 * md) ^ f) + grp) + 8 * (s16 & 1);
+    } else {
+      const int kl = 4 * g + (s16 >> 2);
+      const int f = vswz<false>(kl);
+#pragma unroll
+      for (int md = 0; md < NMD; ++md)
+        vrd[md] = kl * C::VROW + 16 * (((4 * md) ^ f) + 2 * grp + ((s16 >> 1) & 1)) +
+                  8 * (s16 & 1);
+    }
+  }
+
   auto load_frag = [&](int j, const char* ks_, const char* vs_) -> Frag {
     if (j < NPV) {                       // V^T rows 32md.., keys of block nb / step kk
-      const int md = j % NMD, row = 32 * md + l32;
-      const char* rp = vs_ + row * C::VROW;
+      const int md = j % NMD;
       if constexpr (FP8) {
-        const int x = 64 * (j / NMD) + 32 * g;
-        const uint4 v0 = *(const uint4*)(rp + vswz<C::VCH>(row, x));
-        const uint4 v1 = *(const uint4*)(rp + vswz<C::VCH>(row, x + 16));
+        const char* rp = vs_ + vrd[md] + 64 * (j / NMD) * C::VROW;
         i32x8 f;
-        f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
-        f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(rp + 16 * r * C::VROW));
+          f[2 * r] = x[0];
+          f[2 * r + 1] = x[1];
+        }
         return f;
       } else {
-        const uint4 a = *(const uint4*)(rp + vswz<C::VCH>(row, 2 * (16 * (j / NMD) + 8 * g)));
-        return *(const Frag*)&a;
+        const char* rp = vs_ + vrd[md] + 16 * (j / NMD) * C::VROW;
+        const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)rp);
+        const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(rp + 8 * C::VROW));
+        const uint2 a = __builtin_bit_cast(uint2, x0), b2 = __builtin_bit_cast(uint2, x1);
+        return __builtin_bit_cast(Frag, make_uint4(a.x, a.y, b2.x, b2.y));
       }
     } else {                             // K rows 32m.., channels of k-step ks
       const int jj = j - NPV, ks = jj / C::MT, m = jj % C::MT;

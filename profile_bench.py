@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import csv
 import json
+import re
 import os
 import subprocess
 import sys
@@ -27,7 +28,9 @@ sys.path.insert(0, ROOT)
 from bench import kernel_source_sha  # noqa: E402
 
 TAG = "attn_fwd_fp8_d128_lse_gauss32k"
-KERNEL = "attn_fwd_kernel<true, 128, 128, 4, true>"
+# the FP8 d128 kernel with LSE, whatever its tile template arguments
+KERNEL = "attn_fwd_kernel<true, 128, *, true>"
+KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, [0-9, ]+, true>")
 # kernel trace: the same step loop bench.py times; counter passes: a shorter loop
 BENCH_KT = ["python", "bench.py", "--profile-only", "--steps", "20", "--warmup", "5"]
 BENCH = ["python", "bench.py", "--profile-only", "--steps", "3", "--warmup", "1"]
@@ -58,11 +61,12 @@ def rocprof(args, prog, raw, name):
 
 def counters(d, match):
     """{dispatch: {counter: value}} and {dispatch: duration_ns} for kernels whose
-    name contains `match`."""
+    name matches `match` (a compiled pattern or a lower-case substring)."""
     vals, dur = {}, {}
     with open(os.path.join(d, "run_counter_collection.csv")) as f:
         for r in csv.DictReader(f):
-            if match not in r["Kernel_Name"].lower() and match not in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            if not (match.search(name) if hasattr(match, "search") else match in name.lower()):
                 continue
             i = int(r["Dispatch_Id"])
             vals.setdefault(i, {}).setdefault(r["Counter_Name"], 0.0)
@@ -91,13 +95,15 @@ def main() -> int:
              f"# kernel source sha: {kernel_source_sha()}", "",
              f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
     attn_avg_ns = None
+    kernel_name = KERNEL
     for r in rows:
         name = r["Name"]
         lines.append(f"{name[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.1f} "
                      f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} "
                      f"{float(r['Percentage']):6.2f}")
-        if KERNEL in name:
+        if KERNEL_RE.search(name):
             attn_avg_ns = float(r["AverageNs"])
+            kernel_name = name
     flops = 4.0 * 32 * 32768.0 ** 2 * 128 / 2
     if attn_avg_ns:
         lines += ["", f"attention kernel average {attn_avg_ns/1e3:.1f} us -> "
@@ -110,7 +116,7 @@ def main() -> int:
     cmds = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         d, cmds[f"attn_{ctr}"] = rocprof(["--pmc", ctr], BENCH, raw, f"attn_{ctr}")
-        v, _ = counters(d, KERNEL)
+        v, _ = counters(d, KERNEL_RE)
         res[f"attn_{ctr}_kib"] = mean_over(v, ctr)
         d, cmds[f"copy_{ctr}"] = rocprof(["--pmc", ctr], COPY, raw, f"copy_{ctr}")
         v, _ = counters(d, "copy")
@@ -121,7 +127,7 @@ def main() -> int:
     fetch_b = res["attn_FETCH_SIZE_kib"] * 1024 * f_fetch
     write_b = res["attn_WRITE_SIZE_kib"] * 1024 * f_write
     alg = 32768 * 32 * 128 + 2 * 32768 * 8 * 128 + 32768 * 32 * 128 * 2 + 32 * 32768 * 4
-    traffic = {TAG: {"source_sha": kernel_source_sha(), "kernel": KERNEL,
+    traffic = {TAG: {"source_sha": kernel_source_sha(), "kernel": kernel_name,
                      "hbm_bytes_per_launch": round(fetch_b + write_b),
                      "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
                      "algorithmic_bytes": alg,
@@ -131,7 +137,7 @@ def main() -> int:
     with open(os.path.join(out, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     with open(os.path.join(out, f"{TAG}_traffic.txt"), "w") as f:
-        f.write(f"# HBM traffic per launch of {KERNEL} (gauss32k, with LSE)\n")
+        f.write(f"# HBM traffic per launch of {kernel_name} (gauss32k, with LSE)\n")
         for k, c in cmds.items():
             f.write(f"# {k}: {c}\n")
         f.write(f"copy of {COPY_MIB} MiB: FETCH_SIZE {res['copy_FETCH_SIZE_kib']:.0f} KiB, "
@@ -148,7 +154,7 @@ def main() -> int:
     for i, p in enumerate(SQ_PASSES):
         d, c = rocprof(["--pmc", *p], BENCH, raw, f"sq{i}")
         cmdl.append(c)
-        v, dur = counters(d, KERNEL)
+        v, dur = counters(d, KERNEL_RE)
         for k in p:
             agg[k] = mean_over(v, k)
         agg.setdefault("dur_ns", sum(dur.values()) / len(dur))
@@ -156,7 +162,7 @@ def main() -> int:
     gui = agg["GRBM_GUI_ACTIVE"] / xcd                     # cycles per XCD
     sclk = gui / agg["dur_ns"] * 1e3
     simd_cycles = gui * cus * simds
-    lines = [f"# SQ/GRBM counters, {KERNEL}, gauss32k with LSE (means per dispatch)"]
+    lines = [f"# SQ/GRBM counters, {kernel_name}, gauss32k with LSE (means per dispatch)"]
     lines += [f"# command: {c}" for c in cmdl]
     lines += [f"{k:32s} {v:16.0f}" for k, v in agg.items()]
     lines += ["", "derived:",

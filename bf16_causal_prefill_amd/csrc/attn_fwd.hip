@@ -8,9 +8,10 @@
 //
 // Work split.  A workgroup owns NW*32 consecutive queries of one (batch, head); each of
 // its NW waves owns 32 of them.  The workgroup walks the key axis in tiles of BN keys
-// up to its causal diagonal; each K/V tile is copied HBM -> registers -> LDS once per
-// workgroup (double buffered: the loads of tile j+1 are in flight while tile j is
-// used) and every wave reads its matrix operands from LDS.  The launch asks for two
+// up to its causal diagonal; each K/V tile is copied HBM -> LDS once per workgroup by
+// the buffer loads' direct-to-LDS mode (no registers involved; the copy of tile j+2 is
+// in flight while tiles j and j+1 are used) and every wave reads its matrix operands
+// from LDS.  The launch asks for two
 // waves per SIMD, so while one wave waits on its matrix instructions the other issues
 // its softmax arithmetic.
 //
@@ -78,24 +79,24 @@ struct Cfg {
   static constexpr int EB = FP8 ? 1 : 2;            // bytes per element
   static constexpr int NT = NW * 64;                 // threads per workgroup
   static constexpr int BM = NW * 32;                 // queries per workgroup
-  static constexpr int KRB = DQK * EB;               // K row bytes
-  static constexpr int KROW = KRB + 16;              // padded LDS row (bank spread)
+  static constexpr int KRB = DQK * EB;               // K row bytes = LDS row (unpadded)
   static constexpr int R16 = KRB / 16;               // 16-byte chunks per K row
-  static constexpr int KCH = BN * R16;               // chunks per K tile
-  static constexpr int KPT = (KCH + NT - 1) / NT;    // K chunks per thread
   static constexpr int VROW = DV * EB;               // LDS row of the V tile (one key)
   static constexpr int VCPR = VROW / 16;             // 16-byte chunks per V row
-  static constexpr int VCH = BN * VCPR;              // chunks per V tile
-  static constexpr int VPT = (VCH + NT - 1) / NT;    // V chunks per thread
-  static constexpr int K_BYTES = BN * KROW;
+  static constexpr int K_BYTES = BN * KRB;
   static constexpr int V_BYTES = BN * VROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int NSTAGE = 3;                   // K/V tiles resident at once
-  static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int KDMA = K_BYTES / (1024 * NW);  // 1 KiB direct copies per wave, K
+  static constexpr int VDMA = V_BYTES / (1024 * NW);  // and V
+  static constexpr int NKS = 3;                      // K tiles resident in LDS
+  static constexpr int NVS = 4;                      // V tiles resident in LDS
+  static constexpr int LDS = NKS * K_BYTES + NVS * V_BYTES;
   static constexpr int KS = FP8 ? DQK / 64 : DQK / 16;  // MFMA k-steps of Q K^T
   static constexpr int MT = BN / 32;                 // 32-key M-tiles of S^T
   static constexpr int NB = BN / 64;                 // 64-key blocks
   static_assert(BN % 64 == 0, "key tile must be a multiple of 64");
+  static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0,
+                "each wave copies whole 1 KiB blocks of every tile");
+  static_assert(LDS <= 160 * 1024, "LDS budget of a workgroup");
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
 };
 
@@ -107,6 +108,51 @@ struct Cfg {
 template <bool FP8>
 __device__ __forceinline__ int vswz(int key) {
   return FP8 ? 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1) : 4 * (key & 3);
+}
+
+// The 16-byte chunks of key row r of the LDS K tile are XOR-permuted by kswz<R16>(r)
+// (R16 = chunks per row).  An MFMA operand read makes 16 lanes fetch the same chunk of
+// 16 consecutive rows; with unpadded rows those would share a handful of banks, the
+// permutation spreads them over all 16 4-bank groups.  It never leaves the row (for
+// 12 and 24 chunks it permutes within aligned groups of 4 or 8).
+template <int R16>
+__device__ __forceinline__ int kswz(int row) {
+  static_assert(R16 == 8 || R16 == 12 || R16 == 16 || R16 == 24, "K row size");
+  if (R16 == 16) return row & 15;
+  if (R16 == 12) return (row >> 2) & 3;
+  return (row >> 1) & 7;
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// lds_addr + 16 i.  `rsrc` is a raw buffer descriptor (reads past its range return
+// zeros), `voff` the lane's byte offset in it.  Written as an instruction the compiler
+// does not model, so it neither waits for these copies at every barrier nor before LDS
+// reads of other stages: the caller waits with s_waitcnt vmcnt before publishing.
+__device__ __forceinline__ void copy16_to_lds(i32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+#endif
+}
+
+// A raw buffer descriptor for `bytes` bytes at `base` (wave-uniform).
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // Maps the flat workgroup id to (batch, query head, query tile).  Heaviest causal
@@ -215,67 +261,42 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS (double buffered) -----------
-  // Buffer loads: each thread copies the same byte offsets of every tile; keys past N
-  // in the last tile read as zeros (they are masked: key > every query row).
-  uint4 kreg[C::KPT];
-  uint4 vreg[C::VPT];
-  uint32_t koff[C::KPT], voff[C::VPT];
+  // ---- K/V tile copies: global -> LDS -------------------------------------------
+  // Each wave copies KDMA (K) and VDMA (V) 1 KiB blocks of every tile; lane i of block q
+  // fills LDS chunk 64q + i of the tile, i.e. row (64q + i) / R16 at position
+  // (64q + i) % R16, with the global chunk that the row's swizzle puts there.  The
+  // descriptors cover this (b, kv head)'s keys 0..N-1, so keys past N read as zeros
+  // (they are masked: key > every query row).
+  uint32_t kdoff[C::KDMA], vdoff[C::VDMA];
 #pragma unroll
-  for (int cix = 0; cix < C::KPT; ++cix) {
-    const int cc = tid + cix * C::NT;
-    const int row = cc / C::R16, col = cc - row * C::R16;
-    koff[cix] = (uint32_t)row * (uint32_t)kstride + (uint32_t)col * 16u;
+  for (int i = 0; i < C::KDMA; ++i) {
+    const int cc = (wave * C::KDMA + i) * 64 + lane;
+    const int row = cc / C::R16, pos = cc - row * C::R16;
+    kdoff[i] = (uint32_t)row * (uint32_t)kstride + 16u * (uint32_t)(pos ^ kswz<C::R16>(row));
   }
 #pragma unroll
-  for (int u = 0; u < C::VPT; ++u) {
-    const int cc = tid + u * C::NT;
-    const int row = cc / C::VCPR, col = cc - row * C::VCPR;
-    voff[u] = (uint32_t)row * (uint32_t)vstride + (uint32_t)col * 16u;
+  for (int i = 0; i < C::VDMA; ++i) {
+    const int cc = (wave * C::VDMA + i) * 64 + lane;
+    const int row = cc / C::VCPR, pos = cc - row * C::VCPR;
+    vdoff[i] = (uint32_t)row * (uint32_t)vstride + 16u * (uint32_t)(pos ^ vswz<FP8>(row));
   }
+  const i32x4_t krsrc = buffer_rsrc(kbase, (uint32_t)((N - 1) * kstride + C::KRB));
+  const i32x4_t vrsrc = buffer_rsrc(vbase, (uint32_t)((N - 1) * vstride + C::VROW));
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  char* const kst = lds;                                // NKS K stages
+  char* const vst = lds + C::NKS * C::K_BYTES;          // NVS V stages
+  constexpr int NDMA = C::KDMA + C::VDMA;               // copies per wave per tile
 
-  // One descriptor per tensor for the whole key range of this (b, kv head); a tile is
-  // addressed by adding its byte offset to the per-thread offsets.  The range ends at
-  // key N-1, so the last tile's keys past N read as zeros.
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)kbase, (short)0, (N - 1) * (int)kstride + C::KRB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, (N - 1) * (int)vstride + DV * C::EB, 0x00020000);
-
-  auto load_tile = [&](int kt) {
+  auto copy_tile = [&](int kt) {
     const uint32_t kt_off = (uint32_t)kt * BN * (uint32_t)kstride;
     const uint32_t vt_off = (uint32_t)kt * BN * (uint32_t)vstride;
+    const uint32_t kl = lds_base + (uint32_t)((kt % C::NKS) * C::K_BYTES + wave * C::KDMA * 1024);
+    const uint32_t vl = lds_base + (uint32_t)(C::NKS * C::K_BYTES + (kt % C::NVS) * C::V_BYTES +
+                                              wave * C::VDMA * 1024);
 #pragma unroll
-    for (int cix = 0; cix < C::KPT; ++cix) {
-      if (C::KCH % C::NT != 0 && tid + cix * C::NT >= C::KCH) break;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(krsrc, koff[cix] + kt_off, 0, 0);
-      kreg[cix] = *(const uint4*)&x;
-    }
+    for (int i = 0; i < C::KDMA; ++i) copy16_to_lds(krsrc, kdoff[i] + kt_off, kl + 1024u * i);
 #pragma unroll
-    for (int u = 0; u < C::VPT; ++u) {
-      if (C::VCH % C::NT != 0 && tid + u * C::NT >= C::VCH) break;
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff[u] + vt_off, 0, 0);
-      vreg[u] = *(const uint4*)&x;
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    char* ks_ = lds + buf * C::STAGE;
-    char* vs_ = ks_ + C::K_BYTES;
-#pragma unroll
-    for (int cix = 0; cix < C::KPT; ++cix) {
-      const int cc = tid + cix * C::NT;
-      if (C::KCH % C::NT != 0 && cc >= C::KCH) break;
-      const int row = cc / C::R16, col = cc - row * C::R16;
-      *(uint4*)(ks_ + row * C::KROW + col * 16) = kreg[cix];
-    }
-#pragma unroll
-    for (int u = 0; u < C::VPT; ++u) {
-      const int cc = tid + u * C::NT;
-      if (C::VCH % C::NT != 0 && cc >= C::VCH) break;
-      const int row = cc / C::VCPR, col = cc - row * C::VCPR;
-      *(uint4*)(vs_ + row * C::VROW + 16 * (col ^ vswz<FP8>(row))) = vreg[u];
-    }
+    for (int i = 0; i < C::VDMA; ++i) copy16_to_lds(vrsrc, vdoff[i] + vt_off, vl + 1024u * i);
   };
 
   // ---- per-query running state ---------------------------------------------------
@@ -301,8 +322,11 @@ void attn_fwd_kernel(FwdParams p) {
   // each per SIMD, run the same sequence half a phase apart, separated by workgroup
   // barriers: while one group issues matrix instructions the other does its softmax
   // arithmetic on the same SIMD, and the matrix group runs at raised issue priority.
-  // Tiles are staged three deep in LDS: tile t+1 is written during MFMA(t), tile t is
-  // read by both groups' S(t) and P(t) V_t, which end before tile t+3 overwrites it.
+  // Copies run two tiles ahead: MFMA(t) starts the copy of tile t+2, into the K stage
+  // of tile t-1 and the V stage of tile t-2, which the other group's MFMA(t-1) (the
+  // last reader) finished before the barrier that opened this phase; hence 3 K and 4 V
+  // stages.  Before each barrier a wave waits for its own copy of tile t+1, so tile
+  // t+1 is complete in LDS when either group's MFMA(t+1) begins.
   const bool grp_b = wave >= NW / 2;
   f32x16 s[C::MT];
   i32x8 pf8[C::NB];             // FP8 P(t-1) operand, one per 64-key block
@@ -355,6 +379,8 @@ void attn_fwd_kernel(FwdParams p) {
     }
   }
 
+  const int kx = kswz<C::R16>(l32);   // swizzle of every K row this lane reads
+
   auto load_frag = [&](int j, const char* ks_, const char* vs_) -> Frag {
     if (j < NPV) {                       // V^T rows 32md.., keys of block nb / step kk
       const int md = j % NMD;
@@ -380,11 +406,17 @@ void attn_fwd_kernel(FwdParams p) {
       }
     } else {                             // K rows 32m.., channels of k-step ks
       const int jj = j - NPV, ks = jj / C::MT, m = jj % C::MT;
-      const char* rp = ks_ + (32 * m + l32) * C::KROW;
+      const char* rp = ks_ + (32 * m + l32) * C::KRB;
       if constexpr (FP8) {
-        return load_i32x8(rp + 64 * ks + 32 * g);
+        const int c0 = 4 * ks + 2 * g;                  // chunks c0, c0 + 1 of the row
+        const uint4 a = *(const uint4*)(rp + 16 * (c0 ^ kx));
+        const uint4 b2 = *(const uint4*)(rp + 16 * ((c0 + 1) ^ kx));
+        i32x8 f;
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b2.x; f[5] = b2.y; f[6] = b2.z; f[7] = b2.w;
+        return f;
       } else {
-        const uint4 a = *(const uint4*)(rp + 2 * (16 * ks + 8 * g));
+        const uint4 a = *(const uint4*)(rp + 16 * ((2 * ks + g) ^ kx));
         return *(const Frag*)&a;
       }
     }
@@ -451,19 +483,14 @@ void attn_fwd_kernel(FwdParams p) {
   };
 
   auto mfma_phase = [&](int t) {
-    const int st_cur = t % C::NSTAGE;
-    const int st_prev = (t + C::NSTAGE - 1) % C::NSTAGE;
-    const int st_next = (t + 1) % C::NSTAGE;
     __builtin_amdgcn_s_setprio(1);
-    // stage tile t+1 (its loads were issued one matrix phase ago), then load tile t+2
-    if (t + 1 < n_kt) store_tile(st_next);
-    if (t + 2 < n_kt) load_tile(t + 2);
+    copy_tile(t + 2);   // past the last tile this reads zeros into a free stage
     // Every matrix phase runs all slots, so the phase is one straight-line schedule.
     // Where a wave has no work the slots are made harmless instead of skipped: the P
     // operand is zero (set by the softmax phase, or initially) and, at t = 0, V is read
     // from the valid tile-0 stage; a Q K^T past the wave's last tile is never used.
-    const char* ks_ = lds + st_cur * C::STAGE;
-    const char* vs_ = lds + (t == 0 ? st_cur : st_prev) * C::STAGE + C::K_BYTES;
+    const char* ks_ = kst + (t % C::NKS) * C::K_BYTES;
+    const char* vs_ = vst + (t == 0 ? 0 : (t - 1) % C::NVS) * C::V_BYTES;
     run_slots.template operator()<0, NPV + NQK>(ks_, vs_);
     if (FP8 && !WANT_LSE) l_run += zrow[0];
     // Pin the scores to this phase: their only readers are in the softmax phase's
@@ -596,24 +623,30 @@ void attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Every matrix phase issues exactly one tile copy (tiles past the end read zeros
+  // into a free stage), so "this wave's copy of tile t+1 has landed" is always the
+  // same wait, vmcnt <= NDMA, and the phases stay free of branches (the compiler
+  // would sink the P V MFMAs into a branch that followed them).
   zero_p();                             // the first matrix phase has no P yet
-  load_tile(0);
-  store_tile(0);
-  // All prologue loads (Q fragments, tile 0) have landed: say so explicitly, so the
-  // loop does not wait on later tiles' loads before its first matrix instruction.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  if (n_kt > 1) load_tile(1);
+  copy_tile(0);
+  // The Q fragments and tile 0 have landed (loads complete in issue order); the
+  // compiler also learns here that nothing it issued is outstanding.
+  wait_vmcnt<0>();
+  copy_tile(1);
   phase_barrier();
   if (grp_b) phase_barrier();           // group B runs half a phase behind group A
 
   for (int t = 0; t <= n_kt; ++t) {
     mfma_phase(t);
+    wait_vmcnt<NDMA>();
     phase_barrier();
     if (t < n_kt) {
       valu_phase(t);
+      wait_vmcnt<NDMA>();
       phase_barrier();
     }
   }
+  wait_vmcnt<0>();                      // no copy into LDS outlives the loop
   if (!grp_b) phase_barrier();          // equal barrier counts in both groups
   __builtin_amdgcn_s_setprio(0);
 
@@ -660,7 +693,7 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
 hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream) {
   if (fp8) {
     if (d_qk == 128) return launch_cfg<true, 128, 128, 8>(p, stream);
-    return launch_cfg<true, 192, 64, 8>(p, stream);
+    return launch_cfg<true, 192, 128, 8>(p, stream);
   }
   if (d_qk == 128) return launch_cfg<false, 128, 64, 8>(p, stream);
   return launch_cfg<false, 192, 64, 8>(p, stream);

@@ -59,6 +59,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -191,7 +192,8 @@ __device__ __forceinline__ float max_halves(float x) {
 }
 
 // An empty instruction that reads x: the value must be computed by this point.
-__device__ __forceinline__ void keep_in_vgprs(const f32x16& x) {
+template <typename T>
+__device__ __forceinline__ void keep_in_vgprs(const T& x) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("" ::"v"(x));
 #endif
@@ -422,7 +424,15 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  f32x16 zrow;   // FP8 Lean P: rounded-code row sums of tile t-1 (element 0)
+  // Row sums by matrix instruction.  A 16x16 MFMA whose B operand is the probability
+  // operand (lane l: query l%32, 32 keys) and whose A operand selects, for output rows
+  // 4i..4i+3 (read by lanes 16i..16i+15), the k-groups of the lanes holding the same
+  // query (lanes l and l+32 of each 32-lane half), leaves in every lane the sum over
+  // both lane halves of its own query.  rsel marks the A entries that are 1.
+  const bool rsel = ((lane >> 2) & 1) == ((lane >> 4) & 1);
+  f32x4 zrow[C::NB];   // FP8 Lean P: rounded-code row sums of tile t-1, per block,
+                       // still scaled by the block's 2^kb (element 0)
+  f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   auto do_mfma = [&](int j, const Frag& f) {
     if (j < NPV) {
       const int md = j % NMD, blk = j / NMD;
@@ -430,16 +440,13 @@ void attn_fwd_kernel(FwdParams p) {
         oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f, pf8[blk], oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
         if (!WANT_LSE && md == NMD - 1) {
-          // row sums of the rounded probabilities: ones^T P^T (one MFMA per block)
-          i32x8 ones;
+          // row sums of the rounded probabilities: one 16x16x128 MFMA per block with
+          // unit scales (the block scale is removed on the VALU below)
+          i32x8 sel;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;   // e4m3 1.0
-          if (blk == 0)
-            zrow = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                ones, pf8[blk], zero16, 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
-          else
-            zrow = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                ones, pf8[blk], zrow, 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
+          for (int e = 0; e < 8; ++e) sel[e] = rsel ? 0x38383838 : 0;   // e4m3 1.0 or 0
+          zrow[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              sel, pf8[blk], zero4, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
         }
       } else {
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pfb[blk], oacc[md], 0, 0, 0);
@@ -492,7 +499,10 @@ void attn_fwd_kernel(FwdParams p) {
     const char* ks_ = kst + (t % C::NKS) * C::K_BYTES;
     const char* vs_ = vst + (t == 0 ? 0 : (t - 1) % C::NVS) * C::V_BYTES;
     run_slots.template operator()<0, NPV + NQK>(ks_, vs_);
-    if (FP8 && !WANT_LSE) l_run += zrow[0];
+    if (FP8 && !WANT_LSE) {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) l_run += __builtin_ldexpf(zrow[nb][0], psc[nb] - 127);
+    }
     // Pin the scores to this phase: their only readers are in the softmax phase's
     // branch, and the compiler would otherwise sink the Q K^T MFMAs past the barrier.
 #pragma unroll
@@ -570,7 +580,9 @@ void attn_fwd_kernel(FwdParams p) {
         psc[nb] = 127 - (int)kbf;
         if constexpr (WANT_LSE) {
           // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
-          // fp32 sum (scale removed) normalises O and gives the log-sum-exp
+          // fp32 sum (scale removed) normalises O and gives the log-sum-exp.  (The
+          // sum stays on the VALU: a matrix instruction issued here would wait for the
+          // matrix pipe, which the other group keeps busy.)
           const float off = nmc + kbf;
           float bs[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums
 #pragma unroll

@@ -580,9 +580,7 @@ void attn_fwd_kernel(FwdParams p) {
         psc[nb] = 127 - (int)kbf;
         if constexpr (WANT_LSE) {
           // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
-          // fp32 sum (scale removed) normalises O and gives the log-sum-exp.  (The
-          // sum stays on the VALU: a matrix instruction issued here would wait for the
-          // matrix pipe, which the other group keeps busy.)
+          // fp32 sum (scale removed) normalises O and gives the log-sum-exp
           const float off = nmc + kbf;
           float bs[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums
 #pragma unroll
@@ -594,8 +592,9 @@ void attn_fwd_kernel(FwdParams p) {
               pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
               bs[j] += pv[j];
             }
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+            // high half first into the word being replaced, so no zeroed register
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], pf8[nb][w], true);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], word, false);
             pf8[nb][w] = word;
           }
           lx_run += __builtin_ldexpf((bs[0] + bs[1]) + (bs[2] + bs[3]), -(int)kbf);

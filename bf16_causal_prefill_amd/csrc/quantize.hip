@@ -8,9 +8,10 @@
 //
 // Kernels, in stream order:
 //   1. clear     descale[] <- 0 (used as the absmax accumulator, as float bits)
-//   2. absmax    per workgroup max |x| over its rows of one head, then an integer
-//                atomicMax on the float bits (non-negative floats order like their
-//                bit patterns), which is order-independent and so deterministic
+//   2. absmax    per workgroup max |x| over a band of whole rows (per head, gathered
+//                in LDS), then one integer atomicMax per head on the float bits
+//                (non-negative floats order like their bit patterns), which is
+//                order-independent and so deterministic
 //   3. encode    reads the absmax, forms the descale and writes the codes
 //   4. finalize  descale[] <- absmax / 448 (1 for an all-zero tensor or head)
 #include <hip/hip_runtime.h>
@@ -21,38 +22,62 @@
 namespace attn {
 
 constexpr int QZ_THREADS = 256;
-constexpr int QZ_ROWS = 64;     // (b, n) rows of one head per workgroup
+constexpr int QZ_LDS_HEADS = 1024;   // per-head maxima kept in LDS up to this many heads
+constexpr int QZ_TARGET_WGS = 1024;  // workgroups per pass (about four per CU)
+
+// Work split shared by both passes.  The tensor is B*N rows of L4 = H*d/4 float4
+// values (head h owns columns h*d4 .. h*d4 + d4-1, d4 = d/4).  A workgroup takes a band
+// of `band` consecutive rows; thread t handles the columns t, t + 256, ... of every row
+// in the band, so each column's head is fixed per thread and the workgroup reads whole
+// rows (contiguous memory) at a time.
 
 __global__ void qz_clear(uint32_t* amax_bits, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) amax_bits[i] = 0u;
 }
 
-// Grid: (ceil(B*N / QZ_ROWS), H).  A row of one head has d floats, read as float4.
+// Bit patterns of non-negative floats order like the values, so maxima are taken as
+// unsigned integers (atomicMax is then exact and order-independent).
 __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict__ x,
-                                                       uint32_t* amax_bits, int rows, int H,
-                                                       int d, int per_head) {
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.x * QZ_ROWS;
-  const int v4 = d >> 2;                       // float4 per row
-  const int total = min(QZ_ROWS, rows - r0) * v4;
-  float m = 0.f;
-  for (int e = threadIdx.x; e < total; e += QZ_THREADS) {
-    const int r = r0 + e / v4, c4 = e - (e / v4) * v4;
-    const float4 val = *(const float4*)(x + ((size_t)r * H + h) * d + 4 * c4);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(val.x), fabsf(val.y)), fmaxf(fabsf(val.z), fabsf(val.w))));
-  }
-  // bit patterns of non-negative floats order like the values, so reduce as integers
-  uint32_t u = __float_as_uint(m);
-  for (int off = 32; off > 0; off >>= 1) u = max(u, (uint32_t)__shfl_xor((int)u, off));
-  __shared__ uint32_t red[QZ_THREADS / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = u;
+                                                       uint32_t* amax_bits, int rows, int L4,
+                                                       int d4, int H, int per_head, int band) {
+  __shared__ uint32_t hmax[QZ_LDS_HEADS];
+  const int nslots = per_head ? min(H, QZ_LDS_HEADS) : 1;
+  for (int i = threadIdx.x; i < nslots; i += QZ_THREADS) hmax[i] = 0u;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t v = red[0];
-    for (int w = 1; w < QZ_THREADS / 64; ++w) v = max(v, red[w]);
-    atomicMax(amax_bits + (per_head ? h : 0), v);
+  const int r0 = blockIdx.x * band;
+  const int r1 = min(rows, r0 + band);
+  uint32_t all = 0u;                       // per-tensor mode: this thread's maximum
+  for (int c = threadIdx.x; c < L4; c += QZ_THREADS) {
+    const float4* col = (const float4*)x + (size_t)r0 * L4 + c;
+    float m0 = 0.f, m1 = 0.f;
+    int r = r0;
+    for (; r + 1 < r1; r += 2) {           // two loads in flight per thread
+      const float4 a = col[0], b = col[L4];
+      col += 2 * (size_t)L4;
+      m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+      m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    }
+    if (r < r1) {
+      const float4 a = col[0];
+      m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    }
+    const uint32_t u = __float_as_uint(fmaxf(m0, m1));
+    if (!per_head) {
+      all = max(all, u);
+    } else {
+      const int h = c / d4;
+      if (h < QZ_LDS_HEADS) atomicMax(&hmax[h], u);
+      else atomicMax(amax_bits + h, u);
+    }
   }
+  if (!per_head) {
+    for (int off = 32; off > 0; off >>= 1) all = max(all, (uint32_t)__shfl_xor((int)all, off));
+    if ((threadIdx.x & 63) == 0) atomicMax(&hmax[0], all);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nslots; i += QZ_THREADS)
+    if (hmax[i] != 0u) atomicMax(amax_bits + i, hmax[i]);
 }
 
 __device__ __forceinline__ float descale_of(uint32_t amax_bits) {
@@ -78,21 +103,31 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
 }
 
 __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
-                                                       uint8_t* __restrict__ out,
+                                                       uint32_t* __restrict__ out,
                                                        const uint32_t* amax_bits, int rows,
-                                                       int H, int d, int per_head) {
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.x * QZ_ROWS;
-  const int v4 = d >> 2;
-  const int total = min(QZ_ROWS, rows - r0) * v4;
-  const float ds = descale_of(amax_bits[per_head ? h : 0]);
-  for (int e = threadIdx.x; e < total; e += QZ_THREADS) {
-    const int r = r0 + e / v4, c4 = e - (e / v4) * v4;
-    const size_t off = ((size_t)r * H + h) * d + 4 * c4;
-    const float4 val = *(const float4*)(x + off);
-    const uint32_t w = e4m3_code(val.x / ds) | (e4m3_code(val.y / ds) << 8) |
-                       (e4m3_code(val.z / ds) << 16) | (e4m3_code(val.w / ds) << 24);
-    *(uint32_t*)(out + off) = w;
+                                                       int L4, int d4, int per_head, int band) {
+  const int r0 = blockIdx.x * band;
+  const int r1 = min(rows, r0 + band);
+  const float ds_t = per_head ? 0.f : descale_of(amax_bits[0]);
+  for (int c = threadIdx.x; c < L4; c += QZ_THREADS) {
+    const float ds = per_head ? descale_of(amax_bits[c / d4]) : ds_t;
+    const float4* src = (const float4*)x + (size_t)r0 * L4 + c;
+    uint32_t* dst = out + (size_t)r0 * L4 + c;
+    int r = r0;
+    for (; r + 1 < r1; r += 2) {
+      const float4 a = src[0], b = src[L4];
+      src += 2 * (size_t)L4;
+      dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
+               (e4m3_code(a.w / ds) << 24);
+      dst[L4] = e4m3_code(b.x / ds) | (e4m3_code(b.y / ds) << 8) | (e4m3_code(b.z / ds) << 16) |
+                (e4m3_code(b.w / ds) << 24);
+      dst += 2 * (size_t)L4;
+    }
+    if (r < r1) {
+      const float4 a = src[0];
+      dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
+               (e4m3_code(a.w / ds) << 24);
+    }
   }
 }
 
@@ -105,13 +140,15 @@ hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, in
                                 int H, int d, int per_head, hipStream_t stream) {
   const int rows = B * N;
   const int ns = per_head ? H : 1;
+  const int L4 = H * (d / 4), d4 = d / 4;
+  const int band = (rows + QZ_TARGET_WGS - 1) / QZ_TARGET_WGS;
+  const int nwg = (rows + band - 1) / band;
   uint32_t* bits = (uint32_t*)descale;
-  const dim3 grid((rows + QZ_ROWS - 1) / QZ_ROWS, H);
   hipLaunchKernelGGL(qz_clear, dim3((ns + 255) / 256), dim3(256), 0, stream, bits, ns);
-  hipLaunchKernelGGL(qz_absmax, grid, dim3(QZ_THREADS), 0, stream, x, bits, rows, H, d,
-                     per_head);
-  hipLaunchKernelGGL(qz_encode, grid, dim3(QZ_THREADS), 0, stream, x, out,
-                     (const uint32_t*)bits, rows, H, d, per_head);
+  hipLaunchKernelGGL(qz_absmax, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4, d4,
+                     H, per_head, band);
+  hipLaunchKernelGGL(qz_encode, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
+                     (const uint32_t*)bits, rows, L4, d4, per_head, band);
   hipLaunchKernelGGL(qz_finalize, dim3((ns + 255) / 256), dim3(256), 0, stream, descale, ns);
   return hipGetLastError();
 }

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "quantize.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "merge.hip", "quantize.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

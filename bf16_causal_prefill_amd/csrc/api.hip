@@ -14,13 +14,14 @@ constexpr long long kMaxElems = 1LL << 31;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int check_shape(int B, int Hq, int Hkv, int N, int d_qk, int d_v, float scale) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return ATTN_E_INVAL;
+int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d_qk, int d_v, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return ATTN_E_INVAL;
   if (Hq % Hkv != 0) return ATTN_E_INVAL;
   if (!(isfinite(scale) && scale > 0.f)) return ATTN_E_INVAL;
   if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ATTN_E_UNSUPPORTED;
-  const long long bn = (long long)B * N;
-  if (bn * Hq * d_qk >= kMaxElems || bn * Hq * d_v >= kMaxElems) return ATTN_E_INVAL;
+  const long long bq = (long long)B * Nq, bk = (long long)B * Nk;
+  if (bq * Hq * d_qk >= kMaxElems || bq * Hq * d_v >= kMaxElems) return ATTN_E_INVAL;
+  if (bk * Hkv * d_qk >= kMaxElems || bk * Hkv * d_v >= kMaxElems) return ATTN_E_INVAL;
   return ATTN_OK;
 }
 
@@ -49,29 +50,27 @@ int launch_status(hipError_t e) {
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int B, int Hq, int Hkv, int N, int d_qk, int d_v,
-                         float softmax_scale, void* stream) {
-  int st = check_shape(B, Hq, Hkv, N, d_qk, d_v, softmax_scale);
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v, float softmax_scale,
+             void* stream) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
+  if (st == ATTN_OK && q_offset < 0) st = ATTN_E_INVAL;
   if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.scale = softmax_scale;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
+  p.scale = softmax_scale;
   return launch_status(attn::launch_attn_fwd(p, false, d_qk, (hipStream_t)stream));
 }
 
-int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
-                        const float* q_descale, const float* k_descale,
-                        const float* v_descale, int descale_per_head, void* o, float* lse,
-                        int B, int Hq, int Hkv, int N, int d_qk, int d_v,
-                        float softmax_scale, void* stream) {
-  int st = check_shape(B, Hq, Hkv, N, d_qk, d_v, softmax_scale);
+int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_descale,
+            const float* k_descale, const float* v_descale, int descale_per_head, void* o,
+            float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v,
+            float softmax_scale, void* stream) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
+  if (st == ATTN_OK && q_offset < 0) st = ATTN_E_INVAL;
   if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
   if (st == ATTN_OK && (!q_descale || !k_descale || !v_descale)) st = ATTN_E_INVAL;
   if (st == ATTN_OK && (descale_per_head != 0 && descale_per_head != 1)) st = ATTN_E_INVAL;
@@ -83,8 +82,61 @@ int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.scale = softmax_scale;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
+  p.scale = softmax_scale;
   return launch_status(attn::launch_attn_fwd(p, true, d_qk, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                         float softmax_scale, void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, N, 0, d_qk, d_v, softmax_scale, stream);
+}
+
+int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                        const float* q_descale, const float* k_descale,
+                        const float* v_descale, int descale_per_head, void* o, float* lse,
+                        int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                        float softmax_scale, void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
+                 N, N, 0, d_qk, d_v, softmax_scale, stream);
+}
+
+int attn_fwd_causal_offset_bf16(const void* q, const void* k, const void* v, void* o,
+                                float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                                int q_offset, int d_qk, int d_v, float softmax_scale,
+                                void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, q_offset, d_qk, d_v, softmax_scale,
+                  stream);
+}
+
+int attn_fwd_causal_offset_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                               const float* q_descale, const float* k_descale,
+                               const float* v_descale, int descale_per_head, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset,
+                               int d_qk, int d_v, float softmax_scale, void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
+                 Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream);
+}
+
+int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
+                        const float* lse_b, void* o, float* lse, int B, int N, int Hq, int d_v,
+                        void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return ATTN_E_INVAL;
+  if (B < 1 || N < 1 || Hq < 1) return ATTN_E_INVAL;
+  if (d_v < 8 || d_v > 512 || (d_v & (d_v - 1)) != 0) return ATTN_E_INVAL;
+  if ((long long)B * N * Hq * d_v >= kMaxElems) return ATTN_E_INVAL;
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16) || !aligned(lse_a, 4) ||
+      !aligned(lse_b, 4) || (lse && !aligned(lse, 4)))
+    return ATTN_E_ALIGN;
+  const int st = check_device();
+  if (st != ATTN_OK) return st;
+  return launch_status(attn::launch_attn_merge(o_a, lse_a, o_b, lse_b, o, lse, B, N, Hq, d_v,
+                                               (hipStream_t)stream));
 }
 
 int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, int H, int d,

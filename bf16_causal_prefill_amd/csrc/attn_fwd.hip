@@ -224,14 +224,14 @@ void attn_fwd_kernel(FwdParams p) {
   int b, h, qt;
   map_block(blockIdx.x, p, b, h, qt);
   const int hkv = h / (p.Hq / p.Hkv);
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk, q_off = p.q_off;
   const int q0 = qt * C::BM;
   const int q0w = q0 + wave * 32;
 
   const size_t kstride = (size_t)p.Hkv * DQK * C::EB;   // bytes between keys
   const size_t vstride = (size_t)p.Hkv * DV * C::EB;
-  const char* kbase = (const char*)p.k + ((size_t)b * N * p.Hkv + hkv) * DQK * C::EB;
-  const char* vbase = (const char*)p.v + ((size_t)b * N * p.Hkv + hkv) * DV * C::EB;
+  const char* kbase = (const char*)p.k + ((size_t)b * Nk * p.Hkv + hkv) * DQK * C::EB;
+  const char* vbase = (const char*)p.v + ((size_t)b * Nk * p.Hkv + hkv) * DV * C::EB;
 
   // Softmax constant in log2 units per raw score unit (descales folded in for FP8).
   float c = p.scale * LOG2E;
@@ -244,13 +244,13 @@ void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- Q^T fragments (B operand), held for the whole key loop -------------------
-  // Rows past N read row N-1 (finite data); their outputs are never stored.
+  // Rows past Nq read row Nq-1 (finite data); their outputs are never stored.
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
   QFrag qf[C::KS];
   {
     const size_t qstride = (size_t)p.Hq * DQK * C::EB;
-    const char* qbase = (const char*)p.q + ((size_t)b * N * p.Hq + h) * DQK * C::EB;
-    const int qrow = min(q0w + l32, N - 1);
+    const char* qbase = (const char*)p.q + ((size_t)b * Nq * p.Hq + h) * DQK * C::EB;
+    const int qrow = min(q0w + l32, Nq - 1);
     const char* rp = qbase + (size_t)qrow * qstride;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -267,8 +267,8 @@ void attn_fwd_kernel(FwdParams p) {
   // Each wave copies KDMA (K) and VDMA (V) 1 KiB blocks of every tile; lane i of block q
   // fills LDS chunk 64q + i of the tile, i.e. row (64q + i) / R16 at position
   // (64q + i) % R16, with the global chunk that the row's swizzle puts there.  The
-  // descriptors cover this (b, kv head)'s keys 0..N-1, so keys past N read as zeros
-  // (they are masked: key > every query row).
+  // descriptors cover this (b, kv head)'s keys 0..Nk-1, so keys past Nk read as zeros
+  // (and are masked).
   uint32_t kdoff[C::KDMA], vdoff[C::VDMA];
 #pragma unroll
   for (int i = 0; i < C::KDMA; ++i) {
@@ -282,8 +282,8 @@ void attn_fwd_kernel(FwdParams p) {
     const int row = cc / C::VCPR, pos = cc - row * C::VCPR;
     vdoff[i] = (uint32_t)row * (uint32_t)vstride + 16u * (uint32_t)(pos ^ vswz<FP8>(row));
   }
-  const i32x4_t krsrc = buffer_rsrc(kbase, (uint32_t)((N - 1) * kstride + C::KRB));
-  const i32x4_t vrsrc = buffer_rsrc(vbase, (uint32_t)((N - 1) * vstride + C::VROW));
+  const i32x4_t krsrc = buffer_rsrc(kbase, (uint32_t)((Nk - 1) * kstride + C::KRB));
+  const i32x4_t vrsrc = buffer_rsrc(vbase, (uint32_t)((Nk - 1) * vstride + C::VROW));
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   char* const kst = lds;                                // NKS K stages
   char* const vst = lds + C::NKS * C::K_BYTES;          // NVS V stages
@@ -312,10 +312,12 @@ void attn_fwd_kernel(FwdParams p) {
                              // BF16: this lane's keys only)
   float lx_run = 0.f;        // FP8 + LSE: exact row sum over this lane's keys
 
-  const int wg_end = min(q0 + C::BM, N);
-  const int n_kt = (wg_end + BN - 1) / BN;                 // tiles the workgroup loads
-  const int w_end = min(q0w + 32, N);
-  const int w_kt = q0w < N ? (w_end + BN - 1) / BN : 0;    // tiles this wave needs
+  // Query row i sees keys 0 .. min(i + q_off, Nk - 1).
+  const int wg_end = min(q0 + C::BM, Nq);
+  const int n_kt = (min(wg_end + q_off, Nk) + BN - 1) / BN;                  // workgroup's tiles
+  const int w_end = min(q0w + 32, Nq);
+  const int w_kt = q0w < Nq ? (min(w_end + q_off, Nk) + BN - 1) / BN : 0;    // this wave's
+  const int w_lim = min(q0w + q_off, Nk - 1);   // last key every row of the wave sees
 
   // ---- ping-pong main loop ----------------------------------------------------------
   // The tile loop alternates a matrix phase, MFMA(t) = S(t) = K_t Q^T plus O += P(t-1)
@@ -528,12 +530,13 @@ void attn_fwd_kernel(FwdParams p) {
       zero_p();
       return;
     }
-    // causal mask on the tile(s) that cross this wave's diagonal
-    if (t * BN + BN - 1 > q0w) {
+    // causal mask on the tile(s) that cross this wave's diagonal or the end of the keys
+    if (t * BN + BN - 1 > w_lim) {
       // element i of M-tile m holds key t*BN + 32m + 4g + off_i, off_i = 8(i/4) + i%4;
-      // it is masked when off_i > d_m = qrow - (t*BN + 32m + 4g).  Select with integer
-      // ops (sign of d_m - off_i) rather than per-element lane-mask compares.
-      const int d0 = q0w + l32 - (t * BN + 4 * g);
+      // it is masked when off_i > d_m = lim - (t*BN + 32m + 4g), lim = the row's last
+      // visible key.  Select with integer ops (sign of d_m - off_i) rather than
+      // per-element lane-mask compares.
+      const int d0 = min(q0w + l32 + q_off, Nk - 1) - (t * BN + 4 * g);
 #pragma unroll
       for (int m = 0; m < C::MT; ++m)
 #pragma unroll
@@ -668,8 +671,8 @@ void attn_fwd_kernel(FwdParams p) {
   if (FP8 && WANT_LSE) l = lx_run + xor32(lx_run);
   const float lsum = l;
   const float inv = (FP8 ? vds : 1.f) / l;
-  if (qrow < N) {
-    __bf16* orow = (__bf16*)p.o + ((size_t)(b * N + qrow) * p.Hq + h) * DV;
+  if (qrow < Nq) {
+    __bf16* orow = (__bf16*)p.o + ((size_t)((size_t)b * Nq + qrow) * p.Hq + h) * DV;
 #pragma unroll
     for (int md = 0; md < DV / 32; ++md)
 #pragma unroll
@@ -680,7 +683,7 @@ void attn_fwd_kernel(FwdParams p) {
         *(bf16x4*)(orow + 32 * md + 8 * r + 4 * g) = ov;
       }
     if (WANT_LSE && g == 0)
-      p.lse[((size_t)b * p.Hq + h) * N + qrow] =
+      p.lse[((size_t)b * p.Hq + h) * Nq + qrow] =
           (m_run * c + __builtin_amdgcn_logf(lsum)) * LN2;
   }
 }
@@ -689,7 +692,7 @@ template <bool FP8, int DQK, int BN, int NW>
 static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   using C = Cfg<FP8, DQK, BN, NW>;
   FwdParams p = p0;
-  p.n_qtiles = (p.N + C::BM - 1) / C::BM;
+  p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto kern = p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, true>

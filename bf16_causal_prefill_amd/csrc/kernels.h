@@ -15,13 +15,21 @@ struct FwdParams {
   const float* kds;
   const float* vds;
   int per_head;
-  int B, Hq, Hkv, N;
+  int B, Hq, Hkv;
+  int Nq, Nk;          // query rows and key rows per (batch, head)
+  int q_off;           // key j is visible to query i iff j <= i + q_off (0 <= q_off <= Nk)
   float scale;
   int n_qtiles;        // filled in by the launcher
 };
 
 // Enqueues the causal forward kernel; d_v is 128 for both supported shapes.
 hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream);
+
+// Enqueues the merge of two partial attentions over disjoint key sets:
+// o = (e^(lse_a - m) o_a + e^(lse_b - m) o_b) / (e^(lse_a - m) + e^(lse_b - m)), lse = m + ln(..).
+hipError_t launch_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
+                             const float* lse_b, void* o, float* lse, int B, int N, int Hq,
+                             int d_v, hipStream_t stream);
 
 // Enqueues the four kernels of absmax e4m3 quantisation.
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,

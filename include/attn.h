@@ -98,6 +98,53 @@ int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
                         float softmax_scale, void* stream);
 
 /*
+ * Causal attention of Nq queries over Nk keys with a query offset: key j is
+ * visible to query i iff j <= i + q_offset.  This is the same computation with
+ * the causal diagonal shifted, for query chunks that follow a KV prefix
+ * (chunked prefill: q_offset = Nk - Nq for the last Nq of Nk positions) and for
+ * a chunk of keys that lies entirely before the queries (q_offset >= Nk - 1:
+ * every key visible).  The pages' kernels stop at Nq = Nk and name
+ * variable-length work as future work (ai-daily-news.org "Qué cubren los
+ * kernels"); this is that extension, with the partials combined by
+ * attn_merge_partials below.
+ *   q (B, Nq, Hq, d_qk), k (B, Nk, Hkv, d_qk), v (B, Nk, Hkv, d_v),
+ *   o (B, Nq, Hq, d_v) bf16, lse (B, Hq, Nq) float32 or NULL.
+ *   q_offset  >= 0; values above Nk act as Nk.  Every query sees key 0.
+ * Everything else (arguments, numerics, errors) as for the entry points above;
+ * attn_fwd_causal_bf16/_fp8 are these with Nq = Nk = N and q_offset = 0.
+ */
+int attn_fwd_causal_offset_bf16(const void* q, const void* k, const void* v,
+                                void* o, float* lse,
+                                int B, int Hq, int Hkv, int Nq, int Nk, int q_offset,
+                                int d_qk, int d_v, float softmax_scale, void* stream);
+
+int attn_fwd_causal_offset_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                               const float* q_descale, const float* k_descale,
+                               const float* v_descale, int descale_per_head,
+                               void* o, float* lse,
+                               int B, int Hq, int Hkv, int Nq, int Nk, int q_offset,
+                               int d_qk, int d_v, float softmax_scale, void* stream);
+
+/*
+ * Merge of two partial attentions of the same queries over disjoint key sets
+ * (e.g. a KV-prefix chunk and the causal chunk, from the offset entry points):
+ *   m   = max(lse_a, lse_b)
+ *   o   = (e^(lse_a-m) o_a + e^(lse_b-m) o_b) / (e^(lse_a-m) + e^(lse_b-m))
+ *   lse = m + ln(e^(lse_a-m) + e^(lse_b-m))
+ * which is the attention over the union of the two key sets.  A partial whose
+ * LSE is -inf carries weight 0 (both -inf: o = 0, lse = -inf).
+ *   o_a, o_b, o   DEVICE bf16 (B, N, Hq, d_v), 16-byte aligned.
+ *   lse_a, lse_b  DEVICE float32 (B, Hq, N); lse (output) may be NULL.
+ *   d_v           a power of two in [8, 512].
+ * Computed in float32, o rounded to nearest even.  Outputs may alias the
+ * inputs (in-place merge).  One kernel is enqueued.
+ */
+int attn_merge_partials(const void* o_a, const float* lse_a,
+                        const void* o_b, const float* lse_b,
+                        void* o, float* lse, int B, int N, int Hq, int d_v,
+                        void* stream);
+
+/*
  * Absmax quantisation of a float32 (B, N, H, d) tensor into e4m3fn codes
  * (kongchang.com "ZYFA 的性能与精度数据": per-tensor or per-head scale
  * factors map values into the e4m3 range).

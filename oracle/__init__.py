@@ -13,7 +13,8 @@ formats    -- exact decoders for bf16 and OCP e4m3fn codes, a round-to-nearest-
               even saturating e4m3 encoder, and absmax quantisation.
 attention  -- the plain definition of causal softmax attention in float64
               (whole-row softmax, no online/tiled evaluation), over all rows or
-              over sampled (b, h, i) rows.
+              over sampled (b, h, i) rows; the same with Nq queries over Nk keys
+              and a query offset; the merge of two partial attentions.
 
 Every function is pinned by the `-m "not gpu"` tests against library routines
 (torch's float8/bfloat16 casts, torch's scaled_dot_product_attention in fp64),
@@ -24,8 +25,9 @@ inputs.  No function here is "parity unpinned".
 from .formats import (bf16_decode, e4m3_decode, e4m3_encode, quantize_e4m3,
                       absmax_descale, encode_with_descale, E4M3_MAX)
 from .attention import (causal_attention, causal_attention_rows, kv_head_of,
-                        visible_keys)
+                        merge_partials, offset_attention, visible_keys)
 
 __all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "absmax_descale",
            "encode_with_descale", "E4M3_MAX",
-           "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys"]
+           "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys",
+           "offset_attention", "merge_partials"]

@@ -20,6 +20,11 @@ Readings where the pages are silent:
 * grouped KV heads: query head h reads KV head floor(h / (Hq / Hkv));
 * LSE: natural log over the scaled scores, shape (B, Hq, N).
 
+Beyond the pages (their kernels stop at Nq == Nk and leave variable-length work
+for later, ai-daily-news.org "Qué cubren los kernels"): offset_attention lets Nq
+queries attend Nk keys with key j visible to query i iff j <= i + q_offset, and
+merge_partials combines two partial attentions over disjoint key sets.
+
 Inputs are float64 arrays of already-decoded values (bf16 or e4m3 codes times
 their descale), in the (B, N, H, d) layout.
 """
@@ -33,20 +38,22 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visible_keys(i: int) -> int:
-    """Number of keys query i may attend to under the causal mask (0..i)."""
-    return i + 1
+def visible_keys(i: int, q_offset: int = 0, n_keys: int | None = None) -> int:
+    """Number of keys query i may attend to: keys 0..i + q_offset, at most n_keys."""
+    n = i + q_offset + 1
+    return n if n_keys is None else min(n, n_keys)
 
 
 def _rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-          i_abs: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+          i_abs: np.ndarray, q_offset: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Whole-row softmax attention for a block of query rows.
 
-    q_rows (R, dqk), k (Nk, dqk), v (Nk, dv), i_abs (R,) absolute query indices.
+    q_rows (R, dqk), k (Nk, dqk), v (Nk, dv), i_abs (R,) query indices; row r sees
+    keys 0 .. min(i_abs[r] + q_offset, Nk - 1).
     """
-    nk = max(visible_keys(int(i)) for i in i_abs)
+    lim = np.array([visible_keys(int(i), q_offset, k.shape[0]) for i in i_abs])
+    nk = int(lim.max())
     s = scale * (q_rows @ k[:nk].T)                           # (R, nk)
-    lim = np.array([visible_keys(int(i)) for i in i_abs])
     mask = np.arange(nk)[None, :] < lim[:, None]
     s = np.where(mask, s, -np.inf)
     m = np.max(s, axis=1, keepdims=True)
@@ -115,3 +122,60 @@ def causal_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: fl
         out_o[idx] = ob
         out_l[idx] = lb
     return out_o, out_l
+
+
+def offset_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                     q_offset: int, block: int = 512) -> tuple[np.ndarray, np.ndarray]:
+    """Nq queries over Nk keys, key j visible to query i iff j <= i + q_offset.
+
+    q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk), v (B,Nk,Hkv,dv), float64; q_offset >= 0 (so
+    every query sees key 0).  Returns O (B,Nq,Hq,dv) and LSE (B,Hq,Nq), float64.
+    causal_attention is the case Nq == Nk, q_offset == 0.
+    """
+    if q_offset < 0:
+        raise ValueError("q_offset must be >= 0")
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Nq, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    o = np.empty((B, Nq, Hq, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            kk = np.ascontiguousarray(k[b, :, g, :])
+            vv = np.ascontiguousarray(v[b, :, g, :])
+            for i0 in range(0, Nq, block):
+                i1 = min(Nq, i0 + block)
+                ob, lb = _rows(q[b, i0:i1, h, :], kk, vv, scale, np.arange(i0, i1), q_offset)
+                o[b, i0:i1, h, :] = ob
+                lse[b, h, i0:i1] = lb
+    return o, lse
+
+
+def merge_partials(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray,
+                   lse_b: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Attention over the union of two disjoint key sets from the two partial
+    attentions over each: o (B,N,Hq,dv), lse (B,Hq,N).  Each partial's softmax is
+    normalised over its own keys, so partial X contributes with weight
+    exp(lse_X) / (exp(lse_a) + exp(lse_b)) and the union's LSE is the log of that
+    denominator.  A partial with LSE -inf (no keys) contributes nothing."""
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(la, lb)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    wa = np.exp(la - safe)
+    wb = np.exp(lb - safe)
+    den = wa + wb
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(den > 0, safe + np.log(np.where(den > 0, den, 1.0)), -np.inf)
+        fa = np.where(den > 0, wa / np.where(den > 0, den, 1.0), 0.0)
+        fb = np.where(den > 0, wb / np.where(den > 0, den, 1.0), 0.0)
+    # weights are per (b, h, n); O is (b, n, h, :)
+    fa = np.transpose(fa, (0, 2, 1))[..., None]
+    fb = np.transpose(fb, (0, 2, 1))[..., None]
+    o = fa * np.asarray(o_a, dtype=np.float64) + fb * np.asarray(o_b, dtype=np.float64)
+    return o, lse

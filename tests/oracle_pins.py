@@ -165,6 +165,96 @@ def pin_rows_match_full():
         assert abs(rl[r] - lse[b, h, i]) < 1e-13
 
 
+def pin_offset_bruteforce():
+    """Nq queries over Nk keys with a query offset: pure-Python loops, 1e-12.
+    Covers chunked prefill (q_offset = Nk - Nq), Nq > Nk, and every key visible."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, d, dv = 1, 4, 2, 5, 3
+    scale = 0.6
+    for Nq, Nk, off in [(4, 11, 7), (9, 5, 0), (6, 8, 2), (5, 6, 9), (7, 7, 0)]:
+        q, k, v = _rand(rng, B, Nq, Hq, d), _rand(rng, B, Nk, Hkv, d), _rand(rng, B, Nk, Hkv, dv)
+        o, lse = oracle.offset_attention(q, k, v, scale, off, block=3)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if j <= i + off]
+                sc = [scale * sum(q[0, i, h, c] * k[0, j, g, c] for c in range(d)) for j in keys]
+                mx = max(sc)
+                ex = [math.exp(x - mx) for x in sc]
+                tot = sum(ex)
+                for c in range(dv):
+                    ref = sum(e * v[0, j, g, c] for e, j in zip(ex, keys)) / tot
+                    assert abs(o[0, i, h, c] - ref) < 1e-12
+                assert abs(lse[0, h, i] - (mx + math.log(tot))) < 1e-12
+
+
+def pin_offset_chunk_identity():
+    """The last Nq rows of causal attention over N positions are the offset attention
+    of those queries over all N keys with q_offset = N - Nq."""
+    rng = np.random.default_rng(22)
+    B, N, Hq, Hkv, d, dv = 2, 70, 4, 2, 16, 8
+    q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, dv)
+    o, lse = oracle.causal_attention(q, k, v, 0.4, block=32)
+    for nq in (1, 23, 70):
+        oo, ll = oracle.offset_attention(q[:, N - nq:], k, v, 0.4, N - nq, block=16)
+        assert np.max(np.abs(oo - o[:, N - nq:])) < 1e-12
+        assert np.max(np.abs(ll - lse[:, :, N - nq:])) < 1e-12
+
+
+def _sdpa_full(q, k, v, scale):
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=False, scale=scale, enable_gqa=True)
+    return out.permute(0, 2, 1, 3).numpy()
+
+
+def pin_offset_all_visible_sdpa():
+    """q_offset >= Nk - 1 leaves every key visible: torch SDPA without a mask (fp64),
+    and the LSE against torch.logsumexp of the unmasked scores."""
+    rng = np.random.default_rng(23)
+    B, Nq, Nk, Hq, Hkv, d, dv = 1, 40, 57, 4, 2, 32, 16
+    q, k, v = _rand(rng, B, Nq, Hq, d), _rand(rng, B, Nk, Hkv, d), _rand(rng, B, Nk, Hkv, dv)
+    for off in (Nk - 1, Nk + 5):
+        o, lse = oracle.offset_attention(q, k, v, 0.2, off)
+        assert np.max(np.abs(o - _sdpa_full(q, k, v, 0.2))) < 1e-12
+        tk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=2)
+        s = 0.2 * torch.einsum("bihc,bjhc->bhij", torch.from_numpy(q), tk)
+        assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+def pin_merge_split():
+    """Splitting the keys of causal attention at P and merging the two partials (all of
+    keys 0..P-1, then keys P.. causally) gives the causal attention of rows P.."""
+    rng = np.random.default_rng(24)
+    B, N, Hq, Hkv, d, dv = 2, 60, 4, 2, 8, 8
+    q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, dv)
+    o, lse = oracle.causal_attention(q, k, v, 0.5)
+    for p in (1, 17, 59):
+        oa, la = oracle.offset_attention(q[:, p:], k[:, :p], v[:, :p], 0.5, p)
+        ob, lb = oracle.offset_attention(q[:, p:], k[:, p:], v[:, p:], 0.5, 0)
+        om, lm = oracle.merge_partials(oa, la, ob, lb)
+        assert np.max(np.abs(om - o[:, p:])) < 1e-12
+        assert np.max(np.abs(lm - lse[:, :, p:])) < 1e-12
+
+
+def pin_merge_closed_forms():
+    """An empty partial (LSE -inf) leaves the other unchanged; two identical partials
+    give the same O and LSE + ln 2; both empty give O = 0, LSE = -inf."""
+    rng = np.random.default_rng(25)
+    o1 = _rand(rng, 1, 5, 3, 4)
+    l1 = _rand(rng, 1, 3, 5)
+    empty = np.full_like(l1, -np.inf)
+    om, lm = oracle.merge_partials(o1, l1, _rand(rng, 1, 5, 3, 4), empty)
+    assert np.array_equal(om, o1) and np.array_equal(lm, l1)
+    om, lm = oracle.merge_partials(o1, l1, o1, l1)
+    assert np.max(np.abs(om - o1)) < 1e-15 and np.max(np.abs(lm - (l1 + math.log(2)))) < 1e-14
+    om, lm = oracle.merge_partials(o1, empty, o1, empty)
+    assert np.all(om == 0) and np.all(lm == -np.inf)
+
+
 ALL_PINS = [pin_bruteforce, pin_sdpa, pin_equal_scores, pin_row_zero, pin_hardmax,
             pin_rows_sum_to_one, pin_causality, pin_gqa_equals_repeated_mha,
-            pin_rows_match_full]
+            pin_rows_match_full, pin_offset_bruteforce, pin_offset_chunk_identity,
+            pin_offset_all_visible_sdpa, pin_merge_split, pin_merge_closed_forms]

@@ -13,7 +13,8 @@ MI355X dense FP8 matrix peak; traffic = HBM bytes per launch from the committed
 rocprofv3 counter summary when it was taken on the current kernel source, else
 null.  `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload.  "extra" holds the other precisions and shapes of the metric (FP8 with
-and without the LSE, BF16, the MLA shape at 32K) timed the same way.
+and without the LSE, BF16, the MLA shape at 32K) timed the same way, and the
+energy per FLOP of the attention kernels from the device's energy counter.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --profile-only [--steps K]   (step loop only, for rocprofv3)
@@ -79,6 +80,58 @@ def time_events(fn, iters: int, warmup: int = 2) -> float:
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / iters
+
+
+def gpu_energy_reader():
+    """A function returning (joules, counter timestamp in s) for the GPU's energy
+    accumulator (amdsmi: counts times the counter resolution in microjoules; the
+    timestamp is when the device last updated it), or None with the reason when it
+    is not readable.  Only one visible GPU is supported."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) != 1:
+            return None, f"{len(hs)} GPUs visible to amdsmi"
+        h = hs[0]
+
+        def read():
+            e = amdsmi.amdsmi_get_energy_count(h)
+            return (e["energy_accumulator"] * e["counter_resolution"] * 1e-6,
+                    e["timestamp"] * 1e-9)
+        read()
+        return read, None
+    except Exception as exc:   # no library, no permission, no counter
+        return None, f"{type(exc).__name__}: {exc}"[:120]
+
+
+def energy_of(fn, flops: float, read, seconds: float = 3.0) -> dict:
+    """Run fn back to back for about `seconds`; the mean power is the energy counter's
+    increase over its own timestamps taken inside the loop (after a settling second,
+    so both readings fall in steady state), and energy per call = power x the
+    measured time per call.  Returns TFLOP/J and the mean power."""
+    import torch
+    t_ms = time_events(fn, 3)                       # ms per call
+    iters = max(20, int(seconds * 1e3 / t_ms))
+    settle = max(1, int(1e3 / t_ms))
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(settle):
+        fn()
+    torch.cuda.synchronize()
+    (e0, s0) = read()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    (e1, s1) = read()
+    watts = (e1 - e0) / (s1 - s0) if s1 > s0 else None
+    per_call_s = (t1 - t0) / iters
+    return {"tflop_per_j": round(flops / (watts * per_call_s) / 1e12, 3) if watts else None,
+            "avg_w": round(watts, 1) if watts else None, "calls": iters,
+            "loop_s": round(t1 - t0, 3), "counter_s": round(s1 - s0, 3),
+            "settle_s": round(t0 - h0, 3)}
 
 
 def cpu_baseline(w, x, n_heads: int):
@@ -222,6 +275,19 @@ def main() -> int:
             extra[tag + "_tflops"] = round(flops / t / 1e9, 1)
         extra["bf16_attn_lse_pct_peak"] = round(
             100 * extra["bf16_attn_lse_tflops"] / PEAK_TFLOPS["bf16"], 2)
+        # energy: the device's energy counter around back-to-back launches
+        read, why = gpu_energy_reader()
+        if read is None:
+            extra["energy"] = {"unavailable": why}
+        else:
+            log("bench: energy runs")
+            extra["energy"] = {
+                "fp8_attn_lse": energy_of(lambda: attn_fp8(True), flops, read),
+                "fp8_attn_nolse": energy_of(lambda: attn_fp8(False), flops, read),
+                "bf16_attn_lse": energy_of(
+                    lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, lse,
+                                                    softmax_scale=w.softmax_scale), flops, read),
+                "source": "amdsmi energy counter of the GPU (whole device), gauss32k"}
         del xb
         wm = workloads.get("mla32k")
         log("bench: generating mla32k inputs")

@@ -475,18 +475,57 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // slots [J0, J1) with an LA-deep operand pipeline
-  auto run_slots = [&]<int J0, int J1>(const char* ks_, const char* vs_) {
+  // FP8 with exact probabilities (LSE requested) has the longer softmax phase, so its
+  // matrix phase takes over the per-block maxima of S(t): it issues the Q K^T MFMAs
+  // first and forms the maxima while its P V MFMAs run (the scores are complete by
+  // then); a tile that needs the causal mask recomputes them after masking.  In the
+  // other variants the two phases are balanced and moving VALU work into the matrix
+  // phase only lengthens it (measured), so they keep P V first and the max in the
+  // softmax phase.
+  constexpr bool MAX_IN_MFMA = FP8 && WANT_LSE;
+  constexpr int NE = 16 * C::MT;          // scores per lane per tile
+  float bmx_pre[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) bmx_pre[nb] = -INFINITY;
+  float pmx[C::NB][4];                    // independent max chains per block
+  auto max_chunk = [&](int p) {           // p-th of NPV chunks of this lane's scores
+#pragma unroll
+    for (int e = (NE * p) / NPV; e < (NE * (p + 1)) / NPV; ++e) {
+      float& acc = pmx[e >> 5][e & 3];
+      acc = fmaxf(acc, s[e >> 4][e & 15]);
+    }
+    if (p == NPV - 1) {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        bmx_pre[nb] = fmaxf(fmaxf(pmx[nb][0], pmx[nb][1]), fmaxf(pmx[nb][2], pmx[nb][3]));
+        if constexpr (FP8) bmx_pre[nb] = max_halves(bmx_pre[nb]);
+      }
+    }
+  };
+
+  // The matrix phase's slots in issue order: with MAX_IN_MFMA the Q K^T MFMAs of tile t
+  // first (slot indices NPV.. of load_frag / do_mfma), then the P V MFMAs of tile t-1
+  // (0..NPV-1), each P V slot also taking a share of the max over S(t); otherwise P V
+  // then Q K^T.  An LA-deep operand pipeline requests slot j+LA's LDS operand while
+  // slot j's MFMA runs.
+  auto run_slots = [&](const char* ks_, const char* vs_) {
+    constexpr int NS = NPV + NQK;
+    auto vs = [](int j) { return !MAX_IN_MFMA ? j : j < NQK ? NPV + j : j - NQK; };
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pmx[nb][e] = -INFINITY;
     Frag fr[LA + 1];
 #pragma unroll
-    for (int j = J0; j < J0 + LA && j < J1; ++j) fr[(j - J0) % (LA + 1)] = load_frag(j, ks_, vs_);
+    for (int j = 0; j < LA; ++j) fr[j % (LA + 1)] = load_frag(vs(j), ks_, vs_);
 #pragma unroll
-    for (int j = J0; j < J1; ++j) {
+    for (int j = 0; j < NS; ++j) {
       // keep the slots in program order: the scheduler would otherwise hoist every
       // operand read to the top of the phase and run out of registers
       __builtin_amdgcn_sched_barrier(0);
-      if (j + LA < J1) fr[(j + LA - J0) % (LA + 1)] = load_frag(j + LA, ks_, vs_);
-      do_mfma(j, fr[(j - J0) % (LA + 1)]);
+      if (j + LA < NS) fr[(j + LA) % (LA + 1)] = load_frag(vs(j + LA), ks_, vs_);
+      do_mfma(vs(j), fr[j % (LA + 1)]);
+      if (MAX_IN_MFMA && j >= NQK) max_chunk(j - NQK);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -500,15 +539,19 @@ void attn_fwd_kernel(FwdParams p) {
     // from the valid tile-0 stage; a Q K^T past the wave's last tile is never used.
     const char* ks_ = kst + (t % C::NKS) * C::K_BYTES;
     const char* vs_ = vst + (t == 0 ? 0 : (t - 1) % C::NVS) * C::V_BYTES;
-    run_slots.template operator()<0, NPV + NQK>(ks_, vs_);
+    run_slots(ks_, vs_);
     if (FP8 && !WANT_LSE) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) l_run += __builtin_ldexpf(zrow[nb][0], psc[nb] - 127);
     }
-    // Pin the scores to this phase: their only readers are in the softmax phase's
-    // branch, and the compiler would otherwise sink the Q K^T MFMAs past the barrier.
+    // Pin the scores and their maxima to this phase (the compiler would otherwise sink
+    // the Q K^T MFMAs, which touch no memory, and the max past the barrier).
 #pragma unroll
     for (int m = 0; m < C::MT; ++m) keep_in_vgprs(s[m]);
+    if constexpr (MAX_IN_MFMA) {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) keep_in_vgprs(bmx_pre[nb]);
+    }
   };
 
   auto zero_p = [&]() {
@@ -530,8 +573,13 @@ void attn_fwd_kernel(FwdParams p) {
       zero_p();
       return;
     }
+    float bmx[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) bmx[nb] = bmx_pre[nb];
     // causal mask on the tile(s) that cross this wave's diagonal or the end of the keys
-    if (t * BN + BN - 1 > w_lim) {
+    // (then the block maxima are taken again over the masked scores)
+    const bool masked = t * BN + BN - 1 > w_lim;
+    if (masked) {
       // element i of M-tile m holds key t*BN + 32m + 4g + off_i, off_i = 8(i/4) + i%4;
       // it is masked when off_i > d_m = lim - (t*BN + 32m + 4g), lim = the row's last
       // visible key.  Select with integer ops (sign of d_m - off_i) rather than
@@ -546,15 +594,16 @@ void attn_fwd_kernel(FwdParams p) {
           s[m][i] = __uint_as_float((bits & ~(uint32_t)keep) | (0xff800000u & (uint32_t)keep));
         }
     }
-    // max over each 64-key block (this lane's 32 keys, then the other lane half's)
-    float bmx[C::NB];
+    if (masked || !MAX_IN_MFMA) {
+      // max over each 64-key block (this lane's 32 keys, then the other lane half's)
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
+      for (int nb = 0; nb < C::NB; ++nb) {
+        float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
 #pragma unroll
-      for (int e = 0; e < 32; ++e) pm[e & 3] = fmaxf(pm[e & 3], s[2 * nb + (e >> 4)][e & 15]);
-      bmx[nb] = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-      if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
+        for (int e = 0; e < 32; ++e) pm[e & 3] = fmaxf(pm[e & 3], s[2 * nb + (e >> 4)][e & 15]);
+        bmx[nb] = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+        if constexpr (FP8) bmx[nb] = max_halves(bmx[nb]);
+      }
     }
     float mx = bmx[0];
 #pragma unroll

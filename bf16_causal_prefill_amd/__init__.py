@@ -15,13 +15,15 @@ import os
 
 __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
            "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8", "attn_merge_partials",
-           "quantize_e4m3", "attn_status_string", "flash_attn_func", "LIB_PATH",
+           "quantize_e4m3", "quantize_e4m3_hadamard", "attn_status_string", "flash_attn_func",
+           "LIB_PATH",
            "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
-                    "attn_merge_partials", "quantize_e4m3", "attn_status_string")
+                    "attn_merge_partials", "quantize_e4m3", "quantize_e4m3_hadamard",
+                    "attn_status_string")
 
 ATTN_OK = 0
 ATTN_E_INVAL = -1
@@ -63,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.attn_merge_partials.restype = i
     L.quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     L.quantize_e4m3.restype = i
+    L.quantize_e4m3_hadamard.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    L.quantize_e4m3_hadamard.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -127,6 +131,15 @@ def quantize_e4m3(x, out, descale, per_head: bool, stream=None) -> None:
     st = load_library().quantize_e4m3(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
                                       int(bool(per_head)), _stream(stream))
     _check(st, "quantize_e4m3")
+
+
+def quantize_e4m3_hadamard(x, out, descale, per_head: bool, stream=None) -> None:
+    """quantize_e4m3 of x rotated by H/sqrt(hb) per block of hb channels (for Q and K);
+    code * descale is the rotated value."""
+    B, N, H, d = (int(s) for s in x.shape)
+    st = load_library().quantize_e4m3_hadamard(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
+                                               int(bool(per_head)), _stream(stream))
+    _check(st, "quantize_e4m3_hadamard")
 
 
 def _dims_qk(q, k, v):

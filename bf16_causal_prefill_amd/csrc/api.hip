@@ -139,8 +139,8 @@ int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
                                                (hipStream_t)stream));
 }
 
-int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, int H, int d,
-                  int per_head, void* stream) {
+static int quantize_impl(const float* x, uint8_t* out, float* descale, int B, int N, int H,
+                         int d, int per_head, int hadamard, void* stream) {
   if (!x || !out || !descale) return ATTN_E_INVAL;
   if (B < 1 || N < 1 || H < 1 || d < 4 || (d & 3) != 0) return ATTN_E_INVAL;
   if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
@@ -149,8 +149,18 @@ int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, in
   if (!aligned(x, 16) || !aligned(out, 4) || !aligned(descale, 4)) return ATTN_E_ALIGN;
   const int st = check_device();
   if (st != ATTN_OK) return st;
-  return launch_status(
-      attn::launch_quantize_e4m3(x, out, descale, B, N, H, d, per_head, (hipStream_t)stream));
+  return launch_status(attn::launch_quantize_e4m3(x, out, descale, B, N, H, d, per_head,
+                                                  hadamard, (hipStream_t)stream));
+}
+
+int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, int H, int d,
+                  int per_head, void* stream) {
+  return quantize_impl(x, out, descale, B, N, H, d, per_head, 0, stream);
+}
+
+int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, int N, int H,
+                           int d, int per_head, void* stream) {
+  return quantize_impl(x, out, descale, B, N, H, d, per_head, 1, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -31,8 +31,9 @@ hipError_t launch_attn_merge(const void* o_a, const float* lse_a, const void* o_
                              const float* lse_b, void* o, float* lse, int B, int N, int Hq,
                              int d_v, hipStream_t stream);
 
-// Enqueues the four kernels of absmax e4m3 quantisation.
+// Enqueues the four kernels of absmax e4m3 quantisation, optionally of the
+// Hadamard-rotated values (hadamard != 0).
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,
-                                int H, int d, int per_head, hipStream_t stream);
+                                int H, int d, int per_head, int hadamard, hipStream_t stream);
 
 }  // namespace attn

@@ -14,7 +14,16 @@
 //                order-independent and so deterministic
 //   3. encode    reads the absmax, forms the descale and writes the codes
 //   4. finalize  descale[] <- absmax / 448 (1 for an all-zero tensor or head)
+//
+// Optional Hadamard rotation (spke.com "ZYFAのFP8アテンションの精度はどのくらいか?":
+// rotating Q and K roughly halves the FP8 input error): the values quantised are
+// x H / sqrt(hb) with H the Sylvester Hadamard matrix of order hb applied to each block
+// of hb channels (hb = the largest power of two dividing d, at most 128).  Q H (K H)^T
+// = Q K^T, so scores are unchanged while outlier channels are spread over the block.
+// Passes 2 and 3 transform the unnormalised blocks in float32 (wht_block) and the
+// normalisation 1/sqrt(hb) goes into the descale, so the codes are those of x H.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -36,11 +45,31 @@ __global__ void qz_clear(uint32_t* amax_bits, int n) {
   if (i < n) amax_bits[i] = 0u;
 }
 
+// Walsh-Hadamard transform (Sylvester order, unnormalised) of a block of hb = 4*hb4
+// consecutive channels held by hb4 consecutive lanes, 4 channels each (hb4 divides 64
+// and blocks start at multiples of hb4 lanes).  Radix-2 butterflies in float32, stage
+// half-sizes 1, 2, 4, ..., hb/2 in that order: the element with the stage bit clear
+// becomes a + b, its partner a - b.  Every lane of a block must be active.
+__device__ __forceinline__ float4 wht_block(float4 v, int hb4, int lane) {
+  const float a0 = v.x + v.y, a1 = v.x - v.y, a2 = v.z + v.w, a3 = v.z - v.w;
+  v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
+  for (int m = 1; m < hb4; m <<= 1) {
+    const float4 q = make_float4(__shfl_xor(v.x, m), __shfl_xor(v.y, m), __shfl_xor(v.z, m),
+                                 __shfl_xor(v.w, m));
+    if (lane & m) v = make_float4(q.x - v.x, q.y - v.y, q.z - v.z, q.w - v.w);
+    else v = make_float4(v.x + q.x, v.y + q.y, v.z + q.z, v.w + q.w);
+  }
+  return v;
+}
+
 // Bit patterns of non-negative floats order like the values, so maxima are taken as
-// unsigned integers (atomicMax is then exact and order-independent).
+// unsigned integers (atomicMax is then exact and order-independent).  With hb4 > 0
+// the values are the Walsh-Hadamard transforms of blocks of 4*hb4 channels.
 __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict__ x,
                                                        uint32_t* amax_bits, int rows, int L4,
-                                                       int d4, int H, int per_head, int band) {
+                                                       int d4, int H, int per_head, int band,
+                                                       int hb4) {
+  const int lane = threadIdx.x & 63;
   __shared__ uint32_t hmax[QZ_LDS_HEADS];
   const int nslots = per_head ? min(H, QZ_LDS_HEADS) : 1;
   for (int i = threadIdx.x; i < nslots; i += QZ_THREADS) hmax[i] = 0u;
@@ -53,13 +82,18 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict_
     float m0 = 0.f, m1 = 0.f;
     int r = r0;
     for (; r + 1 < r1; r += 2) {           // two loads in flight per thread
-      const float4 a = col[0], b = col[L4];
+      float4 a = col[0], b = col[L4];
       col += 2 * (size_t)L4;
+      if (hb4) {
+        a = wht_block(a, hb4, lane);
+        b = wht_block(b, hb4, lane);
+      }
       m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
       m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
     }
     if (r < r1) {
-      const float4 a = col[0];
+      float4 a = col[0];
+      if (hb4) a = wht_block(a, hb4, lane);
       m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
     }
     const uint32_t u = __float_as_uint(fmaxf(m0, m1));
@@ -105,7 +139,9 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
 __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
                                                        uint32_t* __restrict__ out,
                                                        const uint32_t* amax_bits, int rows,
-                                                       int L4, int d4, int per_head, int band) {
+                                                       int L4, int d4, int per_head, int band,
+                                                       int hb4) {
+  const int lane = threadIdx.x & 63;
   const int r0 = blockIdx.x * band;
   const int r1 = min(rows, r0 + band);
   const float ds_t = per_head ? 0.f : descale_of(amax_bits[0]);
@@ -115,8 +151,12 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     uint32_t* dst = out + (size_t)r0 * L4 + c;
     int r = r0;
     for (; r + 1 < r1; r += 2) {
-      const float4 a = src[0], b = src[L4];
+      float4 a = src[0], b = src[L4];
       src += 2 * (size_t)L4;
+      if (hb4) {
+        a = wht_block(a, hb4, lane);
+        b = wht_block(b, hb4, lane);
+      }
       dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
                (e4m3_code(a.w / ds) << 24);
       dst[L4] = e4m3_code(b.x / ds) | (e4m3_code(b.y / ds) << 8) | (e4m3_code(b.z / ds) << 16) |
@@ -124,21 +164,29 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
       dst += 2 * (size_t)L4;
     }
     if (r < r1) {
-      const float4 a = src[0];
+      float4 a = src[0];
+      if (hb4) a = wht_block(a, hb4, lane);
       dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
                (e4m3_code(a.w / ds) << 24);
     }
   }
 }
 
-__global__ void qz_finalize(float* descale, int n) {
+// descale = (absmax / 448) * post, post = 1 or the Hadamard normalisation 1/sqrt(hb).
+__global__ void qz_finalize(float* descale, int n, float post) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) descale[i] = descale_of(__float_as_uint(descale[i]));
+  if (i < n) descale[i] = descale_of(__float_as_uint(descale[i])) * post;
 }
 
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,
-                                int H, int d, int per_head, hipStream_t stream) {
+                                int H, int d, int per_head, int hadamard, hipStream_t stream) {
   const int rows = B * N;
+  // Hadamard block: the largest power of two dividing d, at most 128 (d is a multiple of
+  // 4); in float4 columns, 0 when no rotation is asked for.
+  int hb = 4;
+  while (hb < 128 && d % (2 * hb) == 0) hb *= 2;
+  const int hb4 = hadamard ? hb / 4 : 0;
+  const float post = hadamard ? (float)(1.0 / sqrt((double)hb)) : 1.f;
   const int ns = per_head ? H : 1;
   const int L4 = H * (d / 4), d4 = d / 4;
   const int band = (rows + QZ_TARGET_WGS - 1) / QZ_TARGET_WGS;
@@ -146,10 +194,11 @@ hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, in
   uint32_t* bits = (uint32_t*)descale;
   hipLaunchKernelGGL(qz_clear, dim3((ns + 255) / 256), dim3(256), 0, stream, bits, ns);
   hipLaunchKernelGGL(qz_absmax, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4, d4,
-                     H, per_head, band);
+                     H, per_head, band, hb4);
   hipLaunchKernelGGL(qz_encode, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
-                     (const uint32_t*)bits, rows, L4, d4, per_head, band);
-  hipLaunchKernelGGL(qz_finalize, dim3((ns + 255) / 256), dim3(256), 0, stream, descale, ns);
+                     (const uint32_t*)bits, rows, L4, d4, per_head, band, hb4);
+  hipLaunchKernelGGL(qz_finalize, dim3((ns + 255) / 256), dim3(256), 0, stream, descale, ns,
+                     post);
   return hipGetLastError();
 }
 

@@ -162,6 +162,33 @@ int attn_merge_partials(const void* o_a, const float* lse_a,
 int quantize_e4m3(const float* x, uint8_t* out, float* descale,
                   int B, int N, int H, int d, int per_head, void* stream);
 
+/*
+ * quantize_e4m3 of the Hadamard-rotated tensor, the FP8 pre-step for Q and K
+ * (spke.com "ZYFAのFP8アテンションの精度はどのくらいか?": most of the FP8
+ * error comes from quantising Q, K and V, and a Hadamard rotation of Q and K
+ * roughly halves that input error).  Each block of hb channels of every
+ * (b, n, h) row, hb = the largest power of two dividing d and at most 128
+ * (128 for d = 128, 64 for d = 192), is multiplied by H / sqrt(hb), H the
+ * Sylvester Hadamard matrix of order hb.  That matrix is orthogonal and
+ * symmetric, so rotating both Q and K leaves every score Q.K unchanged while
+ * outlier channels are spread over the block; feed the codes and descales to
+ * attn_fwd_causal_fp8 as usual (V is not rotated).
+ *   The rotated values are the float32 results of radix-2 butterflies on the
+ *   unnormalised block (stage half-sizes 1, 2, 4, ... in that order; the element
+ *   with the stage bit clear becomes a + b, its partner a - b); codes are
+ *   round-to-nearest-even e4m3 of value / (absmax / 448) as in quantize_e4m3,
+ *   and descale = (absmax / 448) * float32(1 / sqrt(hb)), so code * descale is
+ *   the normalised rotated value.  Arguments, limits and errors as for
+ *   quantize_e4m3.  Four kernels are enqueued.
+ *   Whether the rotation lowers the score error depends on the data: with
+ *   synthetic outlier channels shared by Q and K it cuts the FP8 score error
+ *   several-fold; with outliers on different channels of Q and K it raises it,
+ *   since e4m3 keeps a relative precision per element and the rotation mixes
+ *   every channel into each.
+ */
+int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale,
+                           int B, int N, int H, int d, int per_head, void* stream);
+
 /* Static, NUL-terminated name of a status code; never NULL. */
 const char* attn_status_string(int status);
 

@@ -84,10 +84,11 @@ def test_fp8_rejects(kw, code):
     assert _fp8(ba.load_library(), **kw) == code
 
 
-def test_quantize_rejects():
-    lib = ba.load_library()
+@pytest.mark.parametrize("name", ["quantize_e4m3", "quantize_e4m3_hadamard"])
+def test_quantize_rejects(name):
+    fn = getattr(ba.load_library(), name)
     vp = ctypes.c_void_p
-    q = lambda x=A16, o=A16, d_=A16, B=1, N=4, H=2, d=8, ph=0: lib.quantize_e4m3(
+    q = lambda x=A16, o=A16, d_=A16, B=1, N=4, H=2, d=8, ph=0: fn(
         vp(x), vp(o), vp(d_), B, N, H, d, ph, None)
     assert q(x=None) == ba.ATTN_E_INVAL
     assert q(d=6) == ba.ATTN_E_INVAL
@@ -110,3 +111,6 @@ def test_valid_call_without_device_reports_nodevice():
     assert _fp8(lib) == ba.ATTN_E_NODEVICE
     assert lib.quantize_e4m3(ctypes.c_void_p(A16), ctypes.c_void_p(A16), ctypes.c_void_p(A16),
                              1, 4, 2, 8, 0, None) == ba.ATTN_E_NODEVICE
+    assert lib.quantize_e4m3_hadamard(ctypes.c_void_p(A16), ctypes.c_void_p(A16),
+                                      ctypes.c_void_p(A16), 1, 4, 2, 8, 0,
+                                      None) == ba.ATTN_E_NODEVICE

@@ -121,3 +121,97 @@ def test_quantize_error_bound_and_zero_tensor():
     z = np.zeros((1, 4, 2, 8), np.float32)
     zc, zd = oracle.quantize_e4m3(z, True)
     assert np.all(zc == 0) and np.all(zd == 1.0)
+
+
+# ---- Hadamard rotation before quantisation ----------------------------------------
+
+def _sylvester(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+@pytest.mark.parametrize("d", [4, 8, 32, 128, 192, 256])
+def test_hadamard_butterflies_are_the_sylvester_matrix(d):
+    """Small-integer inputs keep every float32 sum exact, so the butterflies must give
+    exactly x times the Sylvester matrix, block by block (scipy's construction too)."""
+    import scipy.linalg
+    hb = formats.hadamard_block(d)
+    assert hb == min(128, d & -d)
+    assert np.array_equal(_sylvester(hb), scipy.linalg.hadamard(hb))
+    rng = np.random.default_rng(d)
+    x = rng.integers(-50, 51, size=(3, 5, d)).astype(np.float32)
+    y = formats.hadamard_unnormalised_fp32(x, hb)
+    ref = (x.astype(np.float64).reshape(3, 5, d // hb, hb) @ _sylvester(hb)).reshape(3, 5, d)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_hadamard_rotation_is_orthogonal():
+    """Normalised, the rotation preserves dot products (so Q.K scores) and is its own
+    inverse."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((64, 128)).astype(np.float32)
+    k = rng.standard_normal((64, 128)).astype(np.float32)
+    r = lambda a: formats.hadamard_unnormalised_fp32(a, 128).astype(np.float64) / np.sqrt(128)
+    s_ref = q.astype(np.float64) @ k.astype(np.float64).T
+    assert np.max(np.abs(r(q) @ r(k).T - s_ref)) < 1e-4
+    twice = formats.hadamard_unnormalised_fp32(formats.hadamard_unnormalised_fp32(q, 128), 128)
+    assert np.max(np.abs(twice / 128.0 - q)) < 1e-5
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_hadamard_codes_decode_to_rotated_values(per_head):
+    """code * descale reproduces the normalised rotated values within e4m3's
+    half-spacing (relative 2^-4, or 2^-10 of the descale below the normal range)."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((1, 40, 3, 192)).astype(np.float32)
+    codes, ds = oracle.quantize_e4m3_hadamard(x, per_head)
+    hb = formats.hadamard_block(192)
+    rot = (x.astype(np.float64).reshape(1, 40, 3, 192 // hb, hb) @ _sylvester(hb)).reshape(x.shape)
+    rot /= np.sqrt(hb)
+    dsb = ds[None, None, :, None] if per_head else ds[0]
+    dec = oracle.e4m3_decode(codes) * dsb
+    err = np.abs(dec - rot)
+    assert np.all(err <= 2.0 ** -4 * np.abs(rot) + 2.0 ** -10 * dsb * 448 / 448 + 1e-6)
+
+
+def _outlier_qk(rng, N, d, coincide):
+    """Per-channel sigma ~ LogNormal(0, 0.5) with 4 channels x20, for Q and K; the
+    outlier channels of K are Q's (coincide) or drawn independently."""
+    out_q = rng.choice(d, 4, replace=False)
+    out_k = out_q if coincide else rng.choice(d, 4, replace=False)
+    sq = np.exp(0.5 * rng.standard_normal(d))
+    sk = np.exp(0.5 * rng.standard_normal(d))
+    sq[out_q] *= 20
+    sk[out_k] *= 20
+    q = (rng.standard_normal((1, N, 1, d)) * sq).astype(np.float32)
+    k = (rng.standard_normal((1, N, 1, d)) * sk).astype(np.float32)
+    return q, k
+
+
+def _fp8_score_error(quant, q, k):
+    s_ref = q[0, :, 0].astype(np.float64) @ k[0, :, 0].astype(np.float64).T
+    (cq, dq), (ck, dk) = quant(q, True), quant(k, True)
+    qd = oracle.e4m3_decode(cq)[0, :, 0] * float(dq[0])
+    kd = oracle.e4m3_decode(ck)[0, :, 0] * float(dk[0])
+    return np.linalg.norm(qd @ kd.T - s_ref) / np.linalg.norm(s_ref)
+
+
+def test_hadamard_reduces_fp8_score_error_when_outliers_align():
+    """The pages' claim, on synthetic outlier channels shared by Q and K (the situation
+    the rotation targets): the FP8 score error relative to the float32 scores falls by
+    more than half.  With independently placed outliers it rises instead (e4m3 keeps a
+    relative precision per element, and the rotation spreads the large products over
+    every channel), which the second half records."""
+    rng = np.random.default_rng(51)
+    q, k = _outlier_qk(rng, 1024, 128, coincide=True)
+    plain = _fp8_score_error(oracle.quantize_e4m3, q, k)
+    rotated = _fp8_score_error(oracle.quantize_e4m3_hadamard, q, k)
+    print(f"aligned outliers: score rel error plain {plain:.4f} rotated {rotated:.4f}")
+    assert rotated < 0.5 * plain
+    q, k = _outlier_qk(rng, 1024, 128, coincide=False)
+    plain = _fp8_score_error(oracle.quantize_e4m3, q, k)
+    rotated = _fp8_score_error(oracle.quantize_e4m3_hadamard, q, k)
+    print(f"independent outliers: score rel error plain {plain:.4f} rotated {rotated:.4f}")
+    assert rotated > plain

@@ -36,7 +36,7 @@ METRIC = "causal prefill attn TFLOP/s @32K (FP8/BF16, d128 & MLA); % MFMA peak"
 # MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x 8192 (fp8) / 4096 (bf16).
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 PAGES_FP8_D128_32K = 2672.0   # the pages' MI355X figure (B, H unstated): context only
-KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "kernels.h")
+KERNEL_SOURCES = ("attn_fwd.h", "attn_fwd_fp8.hip", "attn_common.h", "kernels.h")
 
 
 def log(msg: str) -> None:

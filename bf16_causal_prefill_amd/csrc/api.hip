@@ -62,7 +62,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
-  return launch_status(attn::launch_attn_fwd(p, false, d_qk, (hipStream_t)stream));
+  return launch_status(attn::launch_attn_fwd_bf16(p, d_qk, (hipStream_t)stream));
 }
 
 int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_descale,
@@ -84,7 +84,7 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
-  return launch_status(attn::launch_attn_fwd(p, true, d_qk, (hipStream_t)stream));
+  return launch_status(attn::launch_attn_fwd_fp8(p, d_qk, (hipStream_t)stream));
 }
 
 }  // namespace

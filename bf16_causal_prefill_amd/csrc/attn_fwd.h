@@ -1,4 +1,6 @@
-// Causal forward (prefill) attention kernels for gfx950 (CDNA4), BF16 and FP8 e4m3.
+// Causal forward (prefill) attention kernels for gfx950 (CDNA4), BF16 and FP8 e4m3:
+// the kernel template and its launcher, instantiated by attn_fwd_fp8.hip and
+// attn_fwd_bf16.hip (separate files so that each precision gets its own compile flags).
 //
 // What is computed: O = softmax(mask(Q K^T * scale)) V per (batch, query head), with
 // the query head h reading KV head h / (Hq / Hkv), and the log-sum-exp of each row.
@@ -46,8 +48,11 @@
 // divided by the sum of the same rounded probabilities, taken with one extra MFMA per
 // 64-key block against a matrix of ones, so the approximation's bias cancels in the
 // normalisation.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
 
 #include <type_traits>
 
@@ -377,6 +382,32 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
+  // Block exponent of a 64-key block with maximum bmx, relative to the running max
+  // (nmc = -m c): the block maximum maps into (2^7, 2^8].
+  auto block_exp = [&](float bmx, float nmc) -> float {
+    return fminf(floorf(8.f - fmaf(bmx, c, nmc)), 127.f);
+  };
+  // Exact probabilities of the 8 words of block nb (4 scores each), scaled by the block
+  // exponent (off = nmc + kb), rounded to e4m3 into pf8[nb]; bs[j] receives the sum of
+  // the j-th scores of the words (four independent chains, started from the first word
+  // rather than from zero, which would cost an add of 0 per chain).
+  auto exact_words = [&](int nb, float off, float* bs) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * w + j;
+        pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
+        bs[j] = w == 0 ? pv[j] : bs[j] + pv[j];
+      }
+      // high half first into the word being replaced, so no zeroed register
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], pf8[nb][w], true);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], word, false);
+      pf8[nb][w] = word;
+    }
+  };
+
   // The matrix phase's slots in issue order: with MAX_IN_MFMA the Q K^T MFMAs of tile t
   // first (slot indices NPV.. of load_frag / do_mfma), then the P V MFMAs of tile t-1
   // (0..NPV-1), each P V slot also taking a share of the max over S(t); otherwise P V
@@ -411,8 +442,18 @@ void attn_fwd_kernel(FwdParams p) {
     // Where a wave has no work the slots are made harmless instead of skipped: the P
     // operand is zero (set by the softmax phase, or initially) and, at t = 0, V is read
     // from the valid tile-0 stage; a Q K^T past the wave's last tile is never used.
-    const char* ks_ = kst + (t % C::NKS) * C::K_BYTES;
-    const char* vs_ = vst + (t == 0 ? 0 : (t - 1) % C::NVS) * C::V_BYTES;
+    // FP8: stage offsets as opaque scalars, so that every K fragment address is one
+    // per-lane base plus an immediate (derived from t, the compiler folds them into
+    // negative constants that the LDS offset field cannot hold and adds them per read;
+    // +2-3% measured).  BF16 measured 3-4% slower that way and keeps the plain form.
+    int kso = (t % C::NKS) * C::K_BYTES;
+    int vso = (t == 0 ? 0 : (t - 1) % C::NVS) * C::V_BYTES;
+    if constexpr (FP8) {
+      kso = __builtin_amdgcn_readfirstlane(kso);
+      vso = __builtin_amdgcn_readfirstlane(vso);
+    }
+    const char* ks_ = kst + kso;
+    const char* vs_ = vst + vso;
     run_slots(ks_, vs_);
     if (FP8 && !WANT_LSE) {
 #pragma unroll
@@ -484,7 +525,8 @@ void attn_fwd_kernel(FwdParams p) {
     for (int nb = 1; nb < C::NB; ++nb) mx = fmaxf(mx, bmx[nb]);
     // lazy running max: rescale only when some row's tile max exceeds m by > TAU
     if (__any((mx - m_run) * c > TAU)) {
-      const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
+      // (FP8 block maxima already cover both lane halves of the query)
+      const float m_new = FP8 ? fmaxf(m_run, mx) : fmaxf(m_run, fmaxf(mx, xor32(mx)));
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
       l_run *= alpha;
@@ -501,28 +543,14 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
         // one block exponent per query and 64-key block (both operand scale blocks)
-        const float xmax = fmaf(bmx[nb], c, nmc);
-        const float kbf = fminf(floorf(8.f - xmax), 127.f);
+        const float kbf = block_exp(bmx[nb], nmc);
         psc[nb] = 127 - (int)kbf;
         if constexpr (WANT_LSE) {
           // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
           // fp32 sum (scale removed) normalises O and gives the log-sum-exp
           const float off = nmc + kbf;
-          float bs[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            float pv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 4 * w + j;
-              pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
-              bs[j] += pv[j];
-            }
-            // high half first into the word being replaced, so no zeroed register
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], pf8[nb][w], true);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], word, false);
-            pf8[nb][w] = word;
-          }
+          float bs[4];
+          exact_words(nb, off, bs);
           lx_run += __builtin_ldexpf((bs[0] + bs[1]) + (bs[2] + bs[3]), -(int)kbf);
         } else {
           // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
@@ -625,15 +653,6 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::LDS, stream, p);
   return hipGetLastError();
-}
-
-hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream) {
-  if (fp8) {
-    if (d_qk == 128) return launch_cfg<true, 128, 128, 8>(p, stream);
-    return launch_cfg<true, 192, 128, 8>(p, stream);
-  }
-  if (d_qk == 128) return launch_cfg<false, 128, 64, 8>(p, stream);
-  return launch_cfg<false, 192, 64, 8>(p, stream);
 }
 
 }  // namespace attn

@@ -22,8 +22,9 @@ struct FwdParams {
   int n_qtiles;        // filled in by the launcher
 };
 
-// Enqueues the causal forward kernel; d_v is 128 for both supported shapes.
-hipError_t launch_attn_fwd(const FwdParams& p, bool fp8, int d_qk, hipStream_t stream);
+// Enqueue the causal forward kernel (d_qk 128 or 192; d_v is 128 for both shapes).
+hipError_t launch_attn_fwd_fp8(const FwdParams& p, int d_qk, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const FwdParams& p, int d_qk, hipStream_t stream);
 
 // Enqueues the merge of two partial attentions over disjoint key sets:
 // o = (e^(lse_a - m) o_a + e^(lse_b - m) o_b) / (e^(lse_a - m) + e^(lse_b - m)), lse = m + ln(..).

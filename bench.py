@@ -176,6 +176,57 @@ def copy_only(mib: int, reps: int = 3) -> int:
     return 0
 
 
+def beyond_pages(ba, torch, w, xd, codes, ds, quant) -> dict:
+    """Timings of the entry points past the pages' scope on the same workload: the
+    Hadamard pre-step, chunked prefill (the last CHUNK queries over all keys) with the
+    merge of two partial attentions, and the flash_attn_func wrapper's overhead."""
+    out = {}
+    # Hadamard rotation + quantisation of Q and K (HBM-bound: 2 fp32 reads + 1 code write)
+    def quant_h():
+        for n in "qk":
+            ba.quantize_e4m3_hadamard(xd[n], codes[n], ds[n], per_head=w.fp8_per_head)
+    t = time_events(quant_h, 10)
+    hbytes = sum(xd[n].numel() * 9 for n in "qk")
+    out["quantize_hadamard_qk_ms"] = round(t, 4)
+    out["quantize_hadamard_qk_GBps"] = round(hbytes / t / 1e6, 1)
+    quant()                                  # back to the plain codes
+    # chunked prefill: queries N-CHUNK..N-1 over all N keys (key j visible to query i iff
+    # j <= i + N - CHUNK), FP8 with LSE
+    CHUNK = 4096
+    N, dev = w.N, xd["q"].device
+    off = N - CHUNK
+    qc = codes["q"][:, off:]
+    oc = torch.empty((w.B, CHUNK, w.Hq, w.d_v), device=dev, dtype=torch.bfloat16)
+    lc = torch.empty((w.B, w.Hq, CHUNK), device=dev, dtype=torch.float32)
+    pairs = CHUNK * (off + 1) + CHUNK * (CHUNK - 1) // 2
+    fc = 2.0 * w.B * w.Hq * pairs * (w.d_qk + w.d_v)
+    t = time_events(lambda: ba.attn_fwd_causal_offset_fp8(
+        qc, codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], oc, lc, q_offset=off,
+        softmax_scale=w.softmax_scale, descale_per_head=int(w.fp8_per_head)), 10)
+    out["chunk4k_of_32k_fp8_lse_ms"] = round(t, 4)
+    out["chunk4k_of_32k_fp8_lse_tflops"] = round(fc / t / 1e9, 1)
+    # merge of two partials of that chunk (HBM-bound: reads 2 O + 2 LSE, writes 1 + 1)
+    ob = torch.empty_like(oc)
+    lb = torch.empty_like(lc)
+    om = torch.empty_like(oc)
+    lm = torch.empty_like(lc)
+    mbytes = 3 * (oc.numel() * 2 + lc.numel() * 4)
+    ob.copy_(oc)
+    lb.copy_(lc)
+    t = time_events(lambda: ba.attn_merge_partials(oc, lc, ob, lb, om, lm), 20)
+    out["merge_chunk4k_ms"] = round(t, 4)
+    out["merge_chunk4k_GBps"] = round(mbytes / t / 1e6, 1)
+    # flash_attn_func wrapper (allocates o and lse per call) against the entry point
+    t_entry = time_events(lambda: ba.attn_fwd_causal_offset_fp8(
+        qc, codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], oc, lc, q_offset=off,
+        softmax_scale=w.softmax_scale, descale_per_head=int(w.fp8_per_head)), 10)
+    t_wrap = time_events(lambda: ba.flash_attn_func(
+        qc, codes["k"], codes["v"], softmax_scale=w.softmax_scale, return_lse=True,
+        q_descale=ds["q"], k_descale=ds["k"], v_descale=ds["v"]), 10)
+    out["flash_attn_func_overhead_pct"] = round(100.0 * (t_wrap / t_entry - 1.0), 2)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +340,7 @@ def main() -> int:
                                                     softmax_scale=w.softmax_scale), flops, read),
                 "source": "amdsmi energy counter of the GPU (whole device), gauss32k"}
         del xb
+        extra.update(beyond_pages(ba, torch, w, xd, codes, ds, quant))
         wm = workloads.get("mla32k")
         log("bench: generating mla32k inputs")
         xm = workloads.generate(wm)

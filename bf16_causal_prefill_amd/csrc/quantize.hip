@@ -20,7 +20,8 @@
 // x H / sqrt(hb) with H the Sylvester Hadamard matrix of order hb applied to each block
 // of hb channels (hb = the largest power of two dividing d, at most 128).  Q H (K H)^T
 // = Q K^T, so scores are unchanged while outlier channels are spread over the block.
-// Passes 2 and 3 transform the unnormalised blocks in float32 (wht_block) and the
+// Passes 2 and 3 transform the unnormalised blocks in float32 (wht_block, one kernel
+// instantiation per block size, cross-lane stages on the DPP lane network) and the
 // normalisation 1/sqrt(hb) goes into the descale, so the codes are those of x H.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,43 +33,87 @@ namespace attn {
 
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_LDS_HEADS = 1024;   // per-head maxima kept in LDS up to this many heads
-constexpr int QZ_TARGET_WGS = 1024;  // workgroups per pass (about four per CU)
+// Workgroups per pass (about four per CU) and rows in flight per thread: measured best
+// of 1024/2048/4096 workgroups and 2/4/8 rows on the 16K-32K-row tensors.
+constexpr int QZ_TARGET_WGS = 1024;
+constexpr int QZ_U = 4;
 
 // Work split shared by both passes.  The tensor is B*N rows of L4 = H*d/4 float4
 // values (head h owns columns h*d4 .. h*d4 + d4-1, d4 = d/4).  A workgroup takes a band
 // of `band` consecutive rows; thread t handles the columns t, t + 256, ... of every row
 // in the band, so each column's head is fixed per thread and the workgroup reads whole
-// rows (contiguous memory) at a time.
+// rows (contiguous memory) at a time, QZ_U rows in flight per thread.
 
 __global__ void qz_clear(uint32_t* amax_bits, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) amax_bits[i] = 0u;
 }
 
-// Walsh-Hadamard transform (Sylvester order, unnormalised) of a block of hb = 4*hb4
-// consecutive channels held by hb4 consecutive lanes, 4 channels each (hb4 divides 64
-// and blocks start at multiples of hb4 lanes).  Radix-2 butterflies in float32, stage
-// half-sizes 1, 2, 4, ..., hb/2 in that order: the element with the stage bit clear
-// becomes a + b, its partner a - b.  Every lane of a block must be active.
-__device__ __forceinline__ float4 wht_block(float4 v, int hb4, int lane) {
-  const float a0 = v.x + v.y, a1 = v.x - v.y, a2 = v.z + v.w, a3 = v.z - v.w;
-  v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
-  for (int m = 1; m < hb4; m <<= 1) {
-    const float4 q = make_float4(__shfl_xor(v.x, m), __shfl_xor(v.y, m), __shfl_xor(v.z, m),
-                                 __shfl_xor(v.w, m));
-    if (lane & m) v = make_float4(q.x - v.x, q.y - v.y, q.z - v.z, q.w - v.w);
-    else v = make_float4(v.x + q.x, v.y + q.y, v.z + q.z, v.w + q.w);
+// x[lane ^ M] within the wave (M < 32): quad permutations and row shifts of the DPP
+// lane network for M <= 8 (a row shift serves the 4-lane banks whose partner lies in
+// its direction; two of them, with complementary bank masks, cover the row), a
+// swizzle for M = 16.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int v = __float_as_int(x);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);         // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);         // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xA, false);  // row_shr:4, banks 1,3
+    r = __builtin_amdgcn_update_dpp(r, v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0,2
+  } else if constexpr (M == 8) {
+    r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xC, false);  // row_shr:8, banks 2,3
+    r = __builtin_amdgcn_update_dpp(r, v, 0x108, 0xF, 0x3, false);  // row_shl:8, banks 0,1
+  } else {
+    static_assert(M == 16, "lane_xor: M must be 1, 2, 4, 8 or 16");
+    r = __builtin_amdgcn_ds_swizzle(v, 0x1F | (16 << 10));          // and 31, xor 16
   }
-  return v;
+  return __int_as_float(r);
+}
+
+// Walsh-Hadamard transform (Sylvester order, unnormalised) of a block of hb = 4*HB4
+// consecutive channels held by HB4 consecutive lanes, 4 channels each (blocks start at
+// multiples of HB4 lanes).  Radix-2 butterflies in float32, stage half-sizes 1, 2, 4,
+// ..., hb/2 in that order: the element with the stage bit clear becomes a + b, its
+// partner a - b (written q - v = fma(-1, v, q) in the upper lane, one rounding as for
+// the subtraction).  Every lane of a block must be active.
+template <int M, int HB4>
+__device__ __forceinline__ float4 wht_stages(float4 v, int lane) {
+  if constexpr (M < HB4) {
+    const float sg = (lane & M) ? -1.f : 1.f;
+    v = make_float4(fmaf(sg, v.x, lane_xor<M>(v.x)), fmaf(sg, v.y, lane_xor<M>(v.y)),
+                    fmaf(sg, v.z, lane_xor<M>(v.z)), fmaf(sg, v.w, lane_xor<M>(v.w)));
+    return wht_stages<2 * M, HB4>(v, lane);
+  } else {
+    return v;
+  }
+}
+
+template <int HB4>
+__device__ __forceinline__ float4 wht_block(float4 v, int lane) {
+  if constexpr (HB4 == 0) {
+    return v;
+  } else {
+    const float a0 = v.x + v.y, a1 = v.x - v.y, a2 = v.z + v.w, a3 = v.z - v.w;
+    v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
+    return wht_stages<1, HB4>(v, lane);
+  }
+}
+
+__device__ __forceinline__ float absmax4(float4 a) {
+  return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
 }
 
 // Bit patterns of non-negative floats order like the values, so maxima are taken as
-// unsigned integers (atomicMax is then exact and order-independent).  With hb4 > 0
-// the values are the Walsh-Hadamard transforms of blocks of 4*hb4 channels.
+// unsigned integers (atomicMax is then exact and order-independent).  With HB4 > 0
+// the values are the Walsh-Hadamard transforms of blocks of 4*HB4 channels.
+template <int HB4>
 __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict__ x,
                                                        uint32_t* amax_bits, int rows, int L4,
-                                                       int d4, int H, int per_head, int band,
-                                                       int hb4) {
+                                                       int d4, int H, int per_head, int band) {
   const int lane = threadIdx.x & 63;
   __shared__ uint32_t hmax[QZ_LDS_HEADS];
   const int nslots = per_head ? min(H, QZ_LDS_HEADS) : 1;
@@ -79,24 +124,26 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict_
   uint32_t all = 0u;                       // per-tensor mode: this thread's maximum
   for (int c = threadIdx.x; c < L4; c += QZ_THREADS) {
     const float4* col = (const float4*)x + (size_t)r0 * L4 + c;
-    float m0 = 0.f, m1 = 0.f;
+    float m[QZ_U];
+#pragma unroll
+    for (int u = 0; u < QZ_U; ++u) m[u] = 0.f;
     int r = r0;
-    for (; r + 1 < r1; r += 2) {           // two loads in flight per thread
-      float4 a = col[0], b = col[L4];
-      col += 2 * (size_t)L4;
-      if (hb4) {
-        a = wht_block(a, hb4, lane);
-        b = wht_block(b, hb4, lane);
-      }
-      m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-      m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
+      float4 a[QZ_U];
+#pragma unroll
+      for (int u = 0; u < QZ_U; ++u) a[u] = col[(size_t)u * L4];
+      col += (size_t)QZ_U * L4;
+#pragma unroll
+      for (int u = 0; u < QZ_U; ++u) m[u] = fmaxf(m[u], absmax4(wht_block<HB4>(a[u], lane)));
     }
-    if (r < r1) {
-      float4 a = col[0];
-      if (hb4) a = wht_block(a, hb4, lane);
-      m0 = fmaxf(m0, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    for (; r < r1; ++r) {
+      m[0] = fmaxf(m[0], absmax4(wht_block<HB4>(col[0], lane)));
+      col += L4;
     }
-    const uint32_t u = __float_as_uint(fmaxf(m0, m1));
+    float mm = m[0];
+#pragma unroll
+    for (int u = 1; u < QZ_U; ++u) mm = fmaxf(mm, m[u]);
+    const uint32_t u = __float_as_uint(mm);
     if (!per_head) {
       all = max(all, u);
     } else {
@@ -136,11 +183,16 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
   return sign | (r - (120u << 3));                 // exponent bias 127 -> 7
 }
 
+__device__ __forceinline__ uint32_t e4m3_word(float4 a, float ds) {
+  return e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
+         (e4m3_code(a.w / ds) << 24);
+}
+
+template <int HB4>
 __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
                                                        uint32_t* __restrict__ out,
                                                        const uint32_t* amax_bits, int rows,
-                                                       int L4, int d4, int per_head, int band,
-                                                       int hb4) {
+                                                       int L4, int d4, int per_head, int band) {
   const int lane = threadIdx.x & 63;
   const int r0 = blockIdx.x * band;
   const int r1 = min(rows, r0 + band);
@@ -150,24 +202,19 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     const float4* src = (const float4*)x + (size_t)r0 * L4 + c;
     uint32_t* dst = out + (size_t)r0 * L4 + c;
     int r = r0;
-    for (; r + 1 < r1; r += 2) {
-      float4 a = src[0], b = src[L4];
-      src += 2 * (size_t)L4;
-      if (hb4) {
-        a = wht_block(a, hb4, lane);
-        b = wht_block(b, hb4, lane);
-      }
-      dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
-               (e4m3_code(a.w / ds) << 24);
-      dst[L4] = e4m3_code(b.x / ds) | (e4m3_code(b.y / ds) << 8) | (e4m3_code(b.z / ds) << 16) |
-                (e4m3_code(b.w / ds) << 24);
-      dst += 2 * (size_t)L4;
+    for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
+      float4 a[QZ_U];
+#pragma unroll
+      for (int u = 0; u < QZ_U; ++u) a[u] = src[(size_t)u * L4];
+      src += (size_t)QZ_U * L4;
+#pragma unroll
+      for (int u = 0; u < QZ_U; ++u) dst[(size_t)u * L4] = e4m3_word(wht_block<HB4>(a[u], lane), ds);
+      dst += (size_t)QZ_U * L4;
     }
-    if (r < r1) {
-      float4 a = src[0];
-      if (hb4) a = wht_block(a, hb4, lane);
-      dst[0] = e4m3_code(a.x / ds) | (e4m3_code(a.y / ds) << 8) | (e4m3_code(a.z / ds) << 16) |
-               (e4m3_code(a.w / ds) << 24);
+    for (; r < r1; ++r) {
+      dst[0] = e4m3_word(wht_block<HB4>(src[0], lane), ds);
+      src += L4;
+      dst += L4;
     }
   }
 }
@@ -176,6 +223,15 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
 __global__ void qz_finalize(float* descale, int n, float post) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) descale[i] = descale_of(__float_as_uint(descale[i])) * post;
+}
+
+template <int HB4>
+static void qz_passes(const float* x, uint8_t* out, uint32_t* bits, int rows, int L4, int d4,
+                      int H, int per_head, int band, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL(qz_absmax<HB4>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4,
+                     d4, H, per_head, band);
+  hipLaunchKernelGGL(qz_encode<HB4>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
+                     (const uint32_t*)bits, rows, L4, d4, per_head, band);
 }
 
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,
@@ -193,10 +249,15 @@ hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, in
   const int nwg = (rows + band - 1) / band;
   uint32_t* bits = (uint32_t*)descale;
   hipLaunchKernelGGL(qz_clear, dim3((ns + 255) / 256), dim3(256), 0, stream, bits, ns);
-  hipLaunchKernelGGL(qz_absmax, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4, d4,
-                     H, per_head, band, hb4);
-  hipLaunchKernelGGL(qz_encode, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
-                     (const uint32_t*)bits, rows, L4, d4, per_head, band, hb4);
+  switch (hb4) {
+    case 0: qz_passes<0>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    case 1: qz_passes<1>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    case 2: qz_passes<2>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    case 4: qz_passes<4>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    case 8: qz_passes<8>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    case 16: qz_passes<16>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+    default: qz_passes<32>(x, out, bits, rows, L4, d4, H, per_head, band, nwg, stream); break;
+  }
   hipLaunchKernelGGL(qz_finalize, dim3((ns + 255) / 256), dim3(256), 0, stream, descale, ns,
                      post);
   return hipGetLastError();

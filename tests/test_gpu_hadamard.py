@@ -16,8 +16,8 @@ from gpu_harness import DEV, FP8_REL_FRO, check, gpu_quantize, note, rel_fro, ru
 
 pytestmark = pytest.mark.gpu
 
-# (B, N, H, d, per_head): Hadamard blocks of 128 (d=128), 64 (d=192), 8, 4 (d=4, 12),
-# ragged row counts, per-tensor and per-head descales.
+# (B, N, H, d, per_head): every Hadamard block size (4 .. 128 channels, so every
+# cross-lane butterfly stage), ragged row counts, per-tensor and per-head descales.
 QCASES = [
     (2, 77, 4, 128, True),
     (1, 300, 3, 192, False),
@@ -25,6 +25,10 @@ QCASES = [
     (1, 5, 1, 4, False),
     (1, 65, 5, 12, True),
     (3, 1000, 2, 128, False),
+    (1, 129, 3, 16, True),       # block of 16 channels
+    (2, 70, 2, 32, False),       # 32
+    (1, 90, 5, 96, True),        # 32 (96 = 3 x 32)
+    (1, 257, 2, 64, False),      # 64
 ]
 
 

@@ -11,10 +11,15 @@ its algorithmic FLOPs per launch / its mean launch time, measured with HIP
 events on the stream the library launches on, over the timed steps; peak = the
 MI355X dense FP8 matrix peak; traffic = HBM bytes per launch from the committed
 rocprofv3 counter summary when it was taken on the current kernel source, else
-null.  `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload.  "extra" holds the other precisions and shapes of the metric (FP8 with
-and without the LSE, BF16, the MLA shape at 32K) timed the same way, and the
-energy per FLOP of the attention kernels from the device's energy counter.
+null.  `sclk_mhz` is the shader clock sampled from the device while the FP8
+kernel runs back to back, and `frac_of_clock_adjusted_peak` the kernel's rate
+against the peak at that clock.  `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.  "extra" holds the other precisions and
+shapes of the metric (FP8 with and without the LSE, BF16, the MLA shape at 32K)
+timed the same way, the energy per FLOP of the attention kernels from the
+device's energy counter, and the entry points past the pages' scope (Hadamard
+pre-step, chunked prefill with a query offset, the merge of partial attentions,
+the flash_attn_func wrapper).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --profile-only [--steps K]   (step loop only, for rocprofv3)
@@ -27,6 +32,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -105,7 +111,32 @@ def gpu_energy_reader():
         return None, f"{type(exc).__name__}: {exc}"[:120]
 
 
-def energy_of(fn, flops: float, read, seconds: float = 3.0) -> dict:
+def gpu_clock_reader():
+    """A function returning the GPU's current shader (gfx) clock in MHz, the mean over
+    its XCDs when the device reports one per XCD, or None when not readable."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) != 1:
+            return None
+        h = hs[0]
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            vals = m.get("current_gfxclks")
+            if isinstance(vals, list):
+                vals = [v for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
+                if vals:
+                    return sum(vals) / len(vals)
+            v = m.get("current_gfxclk")
+            return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+        return read if read() is not None else None
+    except Exception:
+        return None
+
+
+def energy_of(fn, flops: float, read, seconds: float = 3.0, clock=None) -> dict:
     """Run fn back to back for about `seconds`; the mean power is the energy counter's
     increase over its own timestamps taken inside the loop (after a settling second,
     so both readings fall in steady state), and energy per call = power x the
@@ -120,10 +151,23 @@ def energy_of(fn, flops: float, read, seconds: float = 3.0) -> dict:
         fn()
     torch.cuda.synchronize()
     (e0, s0) = read()
+    clk, stop = [], threading.Event()
+
+    def poll():                         # the clock every 10 ms until the loop has drained
+        while not stop.wait(0.01):
+            c = clock()
+            if c is not None:
+                clk.append(c)
+    poller = threading.Thread(target=poll, daemon=True) if clock is not None else None
+    if poller is not None:
+        poller.start()
     t0 = time.perf_counter()
     for _ in range(iters):
         fn()
     torch.cuda.synchronize()
+    if poller is not None:
+        stop.set()
+        poller.join()
     t1 = time.perf_counter()
     (e1, s1) = read()
     watts = (e1 - e0) / (s1 - s0) if s1 > s0 else None
@@ -131,7 +175,8 @@ def energy_of(fn, flops: float, read, seconds: float = 3.0) -> dict:
     return {"tflop_per_j": round(flops / (watts * per_call_s) / 1e12, 3) if watts else None,
             "avg_w": round(watts, 1) if watts else None, "calls": iters,
             "loop_s": round(t1 - t0, 3), "counter_s": round(s1 - s0, 3),
-            "settle_s": round(t0 - h0, 3)}
+            "settle_s": round(t0 - h0, 3),
+            "sclk_mhz": round(sum(clk) / len(clk), 1) if clk else None}
 
 
 def cpu_baseline(w, x, n_heads: int):
@@ -304,13 +349,17 @@ def main() -> int:
         log("bench: profile-only run done")
         return 0
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev_attn) / len(ev_attn)
+    attn_all = sorted(a.elapsed_time(b) for a, b in ev_attn)
+    attn_ms = sum(attn_all) / len(attn_all)
+    pct = lambda q: attn_all[min(len(attn_all) - 1, int(q * (len(attn_all) - 1) + 0.5))]
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
     log(f"bench: step {ms_step:.3f} ms ({value:.1f} TFLOP/s); fp8 attention {attn_ms:.3f} ms "
         f"({achieved:.1f} TFLOP/s)")
 
-    extra = {"fp8_attn_lse_ms": round(attn_ms, 4)}
+    extra = {"fp8_attn_lse_ms": round(attn_ms, 4),
+             "fp8_attn_lse_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4),
+                                             round(pct(0.9), 4)]}
     if not args.no_extra:
         t = time_events(lambda: attn_fp8(False), 10)
         extra["fp8_attn_nolse_ms"] = round(t, 4)
@@ -332,12 +381,14 @@ def main() -> int:
             extra["energy"] = {"unavailable": why}
         else:
             log("bench: energy runs")
+            clock = gpu_clock_reader()
             extra["energy"] = {
-                "fp8_attn_lse": energy_of(lambda: attn_fp8(True), flops, read),
-                "fp8_attn_nolse": energy_of(lambda: attn_fp8(False), flops, read),
+                "fp8_attn_lse": energy_of(lambda: attn_fp8(True), flops, read, clock=clock),
+                "fp8_attn_nolse": energy_of(lambda: attn_fp8(False), flops, read, clock=clock),
                 "bf16_attn_lse": energy_of(
                     lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, lse,
-                                                    softmax_scale=w.softmax_scale), flops, read),
+                                                    softmax_scale=w.softmax_scale), flops, read,
+                    clock=clock),
                 "source": "amdsmi energy counter of the GPU (whole device), gauss32k"}
         del xb
         extra.update(beyond_pages(ba, torch, w, xd, codes, ds, quant))
@@ -368,6 +419,8 @@ def main() -> int:
         log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
         cpu = cpu_baseline(w, x, args.cpu_heads)
 
+    # sustained shader clock: sampled from the device during the FP8-with-LSE energy loop
+    sclk = (extra.get("energy", {}).get("fp8_attn_lse") or {}).get("sclk_mhz")
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -389,6 +442,9 @@ def main() -> int:
                      "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp8"], 4),
                      "traffic": traffic_from_profile("attn_fwd_fp8_d128_lse_gauss32k")},
+        "sclk_mhz": sclk,
+        "frac_of_clock_adjusted_peak": (round(achieved / (PEAK_TFLOPS["fp8"] * sclk / 2400.0), 4)
+                                        if sclk else None),
         "cpu_baseline": cpu,
         "context": {"pages_fp8_d128_32k_tflops": PAGES_FP8_D128_32K,
                     "note": "the pages' MI355X kernel figure; B, H and LSE handling unstated"},

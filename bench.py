@@ -364,6 +364,11 @@ def main() -> int:
         t = time_events(lambda: attn_fp8(False), 10)
         extra["fp8_attn_nolse_ms"] = round(t, 4)
         extra["fp8_attn_nolse_tflops"] = round(flops / t / 1e9, 1)
+        # the same fast path writing the LSE of its rounded row sums (consistent with O)
+        t = time_events(lambda: ba.attn_fwd_causal_offset_fp8_rounded_lse(
+            codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], o, lse, q_offset=0,
+            softmax_scale=w.softmax_scale, descale_per_head=int(w.fp8_per_head)), 10)
+        extra["fp8_attn_rounded_lse_tflops"] = round(flops / t / 1e9, 1)
         t = time_events(quant, 10)
         qbytes = sum(x[n].nbytes * 2 + x[n].size for n in "qkv")   # 2 reads + code write
         extra["quantize_qkv_ms"] = round(t, 4)

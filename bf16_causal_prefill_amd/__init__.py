@@ -14,7 +14,8 @@ import math
 import os
 
 __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
-           "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8", "attn_merge_partials",
+           "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
+           "attn_fwd_causal_offset_fp8_rounded_lse", "attn_merge_partials",
            "quantize_e4m3", "quantize_e4m3_hadamard", "attn_status_string", "flash_attn_func",
            "LIB_PATH",
            "EXPORTED_SYMBOLS"]
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
                     "attn_merge_partials", "quantize_e4m3", "quantize_e4m3_hadamard",
-                    "attn_status_string")
+                    "attn_fwd_causal_offset_fp8_rounded_lse", "attn_status_string")
 
 ATTN_OK = 0
 ATTN_E_INVAL = -1
@@ -61,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.attn_fwd_causal_offset_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp,
                                              i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_causal_offset_fp8.restype = i
+    L.attn_fwd_causal_offset_fp8_rounded_lse.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp,
+                                                         i, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_causal_offset_fp8_rounded_lse.restype = i
     L.attn_merge_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
     L.attn_merge_partials.restype = i
     L.quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
@@ -178,6 +182,23 @@ def attn_fwd_causal_offset_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse=
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, off, dqk, dv, scale,
         _stream(stream))
     _check(st, "attn_fwd_causal_offset_fp8")
+
+
+def attn_fwd_causal_offset_fp8_rounded_lse(q, k, v, q_descale, k_descale, v_descale, o, lse,
+                                           q_offset=None, softmax_scale=None,
+                                           descale_per_head=None, stream=None) -> None:
+    """attn_fwd_causal_offset_fp8 on the rounded-probability path, also writing the LSE
+    of the rounded row sum that normalises O (consistent with O, not the exact LSE)."""
+    B, Hq, Hkv, Nq, Nk, dqk, dv = _dims_qk(q, k, v)
+    off = Nk - Nq if q_offset is None else int(q_offset)
+    scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
+    if descale_per_head is None:
+        descale_per_head = int(q_descale.numel() > 1)
+    st = load_library().attn_fwd_causal_offset_fp8_rounded_lse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, off, dqk, dv, scale,
+        _stream(stream))
+    _check(st, "attn_fwd_causal_offset_fp8_rounded_lse")
 
 
 def attn_merge_partials(o_a, lse_a, o_b, lse_b, o, lse=None, stream=None) -> None:

@@ -68,7 +68,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_descale,
             const float* k_descale, const float* v_descale, int descale_per_head, void* o,
             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v,
-            float softmax_scale, void* stream) {
+            float softmax_scale, void* stream, int lse_rounded = 0) {
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
   if (st == ATTN_OK && q_offset < 0) st = ATTN_E_INVAL;
   if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
@@ -82,6 +82,7 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
+  p.lse_rounded = lse_rounded;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
   return launch_status(attn::launch_attn_fwd_fp8(p, d_qk, (hipStream_t)stream));
@@ -121,6 +122,17 @@ int attn_fwd_causal_offset_fp8(const uint8_t* q, const uint8_t* k, const uint8_t
                                int d_qk, int d_v, float softmax_scale, void* stream) {
   return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
                  Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream);
+}
+
+int attn_fwd_causal_offset_fp8_rounded_lse(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                           const float* q_descale, const float* k_descale,
+                                           const float* v_descale, int descale_per_head, void* o,
+                                           float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                                           int q_offset, int d_qk, int d_v, float softmax_scale,
+                                           void* stream) {
+  if (!lse) return ATTN_E_INVAL;
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
+                 Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream, 1);
 }
 
 int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,

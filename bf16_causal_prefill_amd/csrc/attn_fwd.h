@@ -87,11 +87,16 @@ struct Cfg {
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
 };
 
-template <bool FP8, int DQK, int BN, int NW, bool WANT_LSE>
+template <bool FP8, int DQK, int BN, int NW, int LSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   using C = Cfg<FP8, DQK, BN, NW>;
+  // LSE: 0 none; 1 the exact log-sum-exp (FP8: exact probabilities, O normalised by
+  // their fp32 sum); 2 (FP8) the log of the rounded-probability row sum that
+  // normalises the Lean P output, i.e. the LSE consistent with O.
+  constexpr bool WANT_LSE = LSE != 0;
+  constexpr bool EXACT = FP8 && LSE == 1;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -320,7 +325,7 @@ void attn_fwd_kernel(FwdParams p) {
       if constexpr (FP8) {
         oacc[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f, pf8[blk], oacc[md], 0, 0, 0, 0x7f7f7f7f, 0, psc[blk]);
-        if (!WANT_LSE && md == NMD - 1) {
+        if (!EXACT && md == NMD - 1) {
           // row sums of the rounded probabilities: one 16x16x128 MFMA per block with
           // unit scales (the block scale is removed on the VALU below)
           i32x8 sel;
@@ -361,7 +366,7 @@ void attn_fwd_kernel(FwdParams p) {
   // other variants the two phases are balanced and moving VALU work into the matrix
   // phase only lengthens it (measured), so they keep P V first and the max in the
   // softmax phase.
-  constexpr bool MAX_IN_MFMA = FP8 && WANT_LSE;
+  constexpr bool MAX_IN_MFMA = EXACT;
   constexpr int NE = 16 * C::MT;          // scores per lane per tile
   float bmx_pre[C::NB];
 #pragma unroll
@@ -455,7 +460,7 @@ void attn_fwd_kernel(FwdParams p) {
     const char* ks_ = kst + kso;
     const char* vs_ = vst + vso;
     run_slots(ks_, vs_);
-    if (FP8 && !WANT_LSE) {
+    if (FP8 && !EXACT) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) l_run += __builtin_ldexpf(zrow[nb][0], psc[nb] - 127);
     }
@@ -530,7 +535,7 @@ void attn_fwd_kernel(FwdParams p) {
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
       l_run *= alpha;
-      if (WANT_LSE) lx_run *= alpha;
+      if (EXACT) lx_run *= alpha;
 #pragma unroll
       for (int md = 0; md < DV / 32; ++md)
 #pragma unroll
@@ -545,7 +550,7 @@ void attn_fwd_kernel(FwdParams p) {
         // one block exponent per query and 64-key block (both operand scale blocks)
         const float kbf = block_exp(bmx[nb], nmc);
         psc[nb] = 127 - (int)kbf;
-        if constexpr (WANT_LSE) {
+        if constexpr (EXACT) {
           // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
           // fp32 sum (scale removed) normalises O and gives the log-sum-exp
           const float off = nmc + kbf;
@@ -619,7 +624,7 @@ void attn_fwd_kernel(FwdParams p) {
   const int qrow = q0w + l32;
   float l = l_run;
   if (!FP8) l += xor32(l);
-  if (FP8 && WANT_LSE) l = lx_run + xor32(lx_run);
+  if (EXACT) l = lx_run + xor32(lx_run);
   const float lsum = l;
   const float inv = (FP8 ? vds : 1.f) / l;
   if (qrow < Nq) {
@@ -646,8 +651,11 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  auto kern = p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, true>
-                    : attn_fwd_kernel<FP8, DQK, BN, NW, false>;
+  auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0>
+                     : attn_fwd_kernel<FP8, DQK, BN, NW, 1>;
+  if constexpr (FP8) {
+    if (p.lse && p.lse_rounded) kern = attn_fwd_kernel<FP8, DQK, BN, NW, 2>;
+  }
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;

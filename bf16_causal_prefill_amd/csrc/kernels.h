@@ -20,6 +20,7 @@ struct FwdParams {
   int q_off;           // key j is visible to query i iff j <= i + q_off (0 <= q_off <= Nk)
   float scale;
   int n_qtiles;        // filled in by the launcher
+  int lse_rounded;     // FP8: lse from the rounded-probability row sums (consistent with O)
 };
 
 // Enqueue the causal forward kernel (d_qk 128 or 192; d_v is 128 for both shapes).

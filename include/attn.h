@@ -126,6 +126,28 @@ int attn_fwd_causal_offset_fp8(const uint8_t* q, const uint8_t* k, const uint8_t
                                int d_qk, int d_v, float softmax_scale, void* stream);
 
 /*
+ * attn_fwd_causal_offset_fp8 on the fast path (probabilities written straight as
+ * e4m3 codes, O divided by the sum of the rounded probabilities: spke.com
+ * "ブロックごとのスケーリングと丸められた行和"), which also writes the LSE of
+ * that same row sum: lse = m + ln(sum of the rounded probabilities).  That LSE is
+ * the one consistent with O's normaliser, which is what the merge of partial
+ * attentions needs; it differs from the exact log-sum-exp by the rounding of the
+ * probabilities: each rounded probability is within a factor 0.917 .. 1.061 of
+ * the exact one, so the LSE is within 0.087 of the exact LSE (less with many keys
+ * per row), not a substitute where the exact LSE is required.  o is byte-identical to the
+ * lse == NULL call.
+ *   lse       required (NULL returns ATTN_E_INVAL); everything else as for
+ *             attn_fwd_causal_offset_fp8.
+ */
+int attn_fwd_causal_offset_fp8_rounded_lse(const uint8_t* q, const uint8_t* k,
+                                           const uint8_t* v, const float* q_descale,
+                                           const float* k_descale, const float* v_descale,
+                                           int descale_per_head, void* o, float* lse,
+                                           int B, int Hq, int Hkv, int Nq, int Nk,
+                                           int q_offset, int d_qk, int d_v,
+                                           float softmax_scale, void* stream);
+
+/*
  * Merge of two partial attentions of the same queries over disjoint key sets
  * (e.g. a KV-prefix chunk and the causal chunk, from the offset entry points):
  *   m   = max(lse_a, lse_b)

@@ -29,8 +29,8 @@ from bench import kernel_source_sha  # noqa: E402
 
 TAG = "attn_fwd_fp8_d128_lse_gauss32k"
 # the FP8 d128 kernel with LSE, whatever its tile template arguments
-KERNEL = "attn_fwd_kernel<true, 128, *, true>"
-KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, [0-9, ]+, true>")
+KERNEL = "attn_fwd_kernel<true, 128, *, 1>"
+KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1>")
 # kernel trace: the same step loop bench.py times; counter passes: a shorter loop
 BENCH_KT = ["python", "bench.py", "--profile-only", "--steps", "20", "--warmup", "5"]
 BENCH = ["python", "bench.py", "--profile-only", "--steps", "3", "--warmup", "1"]

@@ -114,3 +114,21 @@ def test_valid_call_without_device_reports_nodevice():
     assert lib.quantize_e4m3_hadamard(ctypes.c_void_p(A16), ctypes.c_void_p(A16),
                                       ctypes.c_void_p(A16), 1, 4, 2, 8, 0,
                                       None) == ba.ATTN_E_NODEVICE
+
+
+def test_rounded_lse_entry_requires_lse_and_validates():
+    """attn_fwd_causal_offset_fp8_rounded_lse rejects a NULL lse and bad arguments before
+    touching a device."""
+    lib = ba.load_library()
+    vp = ctypes.c_void_p
+
+    def call(lse=A16, B=1, q=A16, Nq=16, Nk=16, off=0, dqk=128):
+        return lib.attn_fwd_causal_offset_fp8_rounded_lse(
+            vp(q), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), 0, vp(A16), vp(lse), B, 2, 2,
+            Nq, Nk, off, dqk, 128, ctypes.c_float(0.1), None)
+    assert call(lse=None) == ba.ATTN_E_INVAL
+    assert call(B=0) == ba.ATTN_E_INVAL
+    assert call(off=-1) == ba.ATTN_E_INVAL
+    assert call(q=None) == ba.ATTN_E_INVAL
+    assert call(dqk=64) == ba.ATTN_E_UNSUPPORTED
+    assert call(q=A16 + 4) == ba.ATTN_E_ALIGN

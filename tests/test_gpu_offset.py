@@ -241,3 +241,77 @@ def test_flash_attn_func_non_causal_and_rectangular():
         go, gl = _host(o, lse)
         ro, rl = oracle.offset_attention(*dec, scale, off)
         check(f"flash_attn_func causal={causal}", "bf16", go, ro, gl, rl)
+
+
+# ---- the rounded-row-sum LSE (consistent with O on the fast FP8 path) -------------------
+
+def _fp8_inputs(name, B, Nq, Nk, Hq, Hkv, dqk, per_head):
+    q, k, v = _draw(name, B, Nq, Nk, Hq, Hkv, dqk)
+    dev, dec = [], []
+    for x in (q, k, v):
+        cd, dd = gpu_quantize(x, per_head)
+        ch, dh = oracle.quantize_e4m3(x, per_head)
+        assert np.array_equal(cd.cpu().numpy(), ch)
+        dev.append((cd, dd))
+        dec.append(oracle.e4m3_decode(ch) * (dh[None, None, :, None].astype(np.float64)
+                                             if per_head else float(dh[0])))
+    return dev, dec
+
+
+# Each probability the fast path rounds to an e4m3 code (about 8 x + const, the
+# pages' rule) is within a factor of [0.917, 1.061] of the exact one
+# (test_oracle_formats.test_lean_code_ratio_bound derives it), so a row sum of them,
+# and its log, is within ln(1/0.917) = 0.0866 of the exact one; plus the FP8 score
+# error the other LSE tests allow.
+ROUNDED_LSE_BOUND = 0.0866 + 1e-2
+
+
+@pytest.mark.parametrize("case", ["square", "chunk_tail", "mla_chunk", "q_longer"])
+def test_rounded_lse(case):
+    """O is byte-identical to the lse == NULL call; the LSE is within the rounding bound
+    of the oracle's exact LSE."""
+    B, Nq, Nk, off, Hq, Hkv, dqk, per_head = CASES[case]
+    note(f"rounded lse {case}: B={B} Nq={Nq} Nk={Nk} q_offset={off}")
+    dev, dec = _fp8_inputs("rounded-" + case, B, Nq, Nk, Hq, Hkv, dqk, per_head)
+    args = (dev[0][0], dev[1][0], dev[2][0], dev[0][1], dev[1][1], dev[2][1])
+    scale = 1.0 / np.sqrt(dqk)
+    o1, _ = _empty_out(B, Nq, Hq, want_lse=False)
+    o2, l2 = _empty_out(B, Nq, Hq)
+    ba.attn_fwd_causal_offset_fp8(*args, o1, None, q_offset=off, softmax_scale=scale,
+                                  descale_per_head=int(per_head))
+    ba.attn_fwd_causal_offset_fp8_rounded_lse(*args, o2, l2, q_offset=off, softmax_scale=scale,
+                                              descale_per_head=int(per_head))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    ro, rl = oracle.offset_attention(*dec, scale, off)
+    go, gl = _host(o2, l2)
+    check(case, "fp8", go, ro)
+    err = float(np.max(np.abs(gl - rl)))
+    note(f"  rounded LSE max |error| {err:.4f} (bound {ROUNDED_LSE_BOUND:.4f})")
+    assert np.all(np.isfinite(gl)) and err <= ROUNDED_LSE_BOUND
+
+
+def test_rounded_lse_merge_of_split_keys():
+    """The consistent LSE merges: a KV prefix seen in full plus the causal chunk, both on
+    the fast path with rounded LSEs, merged, match attention over all keys (oracle)."""
+    B, N, P, Hq, Hkv, dqk = 1, 500, 300, 4, 2, 128
+    note(f"rounded lse merge: N={N} prefix={P}")
+    dev, dec = _fp8_inputs("rounded-merge", B, N, N, Hq, Hkv, dqk, True)
+    scale = 1.0 / np.sqrt(dqk)
+    qc = dev[0][0][:, P:].contiguous()
+    kp, vp = dev[1][0][:, :P].contiguous(), dev[2][0][:, :P].contiguous()
+    kc, vc = dev[1][0][:, P:].contiguous(), dev[2][0][:, P:].contiguous()
+    ds = (dev[0][1], dev[1][1], dev[2][1])
+    oa, la = _empty_out(B, N - P, Hq)
+    ob, lb = _empty_out(B, N - P, Hq)
+    ba.attn_fwd_causal_offset_fp8_rounded_lse(qc, kp, vp, *ds, oa, la, q_offset=P,
+                                              softmax_scale=scale, descale_per_head=1)
+    ba.attn_fwd_causal_offset_fp8_rounded_lse(qc, kc, vc, *ds, ob, lb, q_offset=0,
+                                              softmax_scale=scale, descale_per_head=1)
+    om, lm = _empty_out(B, N - P, Hq)
+    ba.attn_merge_partials(oa, la, ob, lb, om, lm)
+    torch.cuda.synchronize()
+    ro, rl = oracle.offset_attention(dec[0][:, P:], dec[1], dec[2], scale, P)
+    go, gl = _host(om, lm)
+    check("rounded merge", "fp8", go, ro)
+    assert float(np.max(np.abs(gl - rl))) <= ROUNDED_LSE_BOUND

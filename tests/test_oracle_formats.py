@@ -215,3 +215,17 @@ def test_hadamard_reduces_fp8_score_error_when_outliers_align():
     rotated = _fp8_score_error(oracle.quantize_e4m3_hadamard, q, k)
     print(f"independent outliers: score rel error plain {plain:.4f} rotated {rotated:.4f}")
     assert rotated > plain
+
+
+def test_lean_code_ratio_bound():
+    """The e4m3 code the fast FP8 path writes for a probability 2^x is the integer
+    nearest 8 x + 55.5 (the code of 2^x grows by 8 per doubling, the-ai.news "Drie
+    technieken..."; spke.com "Lean P"), clamped to [0, 0x7E].  Over the range the block
+    exponent keeps the probabilities in (x in [-6, 8]), the decoded code is within a
+    factor [0.917, 1.061] of 2^x; the GPU test of the rounded-row-sum LSE takes its
+    bound, ln(1/0.917), from here."""
+    x = np.linspace(-6.0, 8.0, 400001)
+    code = np.clip(np.rint(8.0 * x + 55.5), 0, 0x7E).astype(np.uint8)
+    r = oracle.e4m3_decode(code) / 2.0 ** x
+    assert 0.9165 <= r.min() <= 0.9175 and 1.0600 <= r.max() <= 1.0612
+    assert np.log(1.0 / r.min()) < 0.0866 + 1e-4

@@ -23,6 +23,9 @@ the flash_attn_func wrapper).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --profile-only [--steps K]   (step loop only, for rocprofv3)
+       python bench.py --profile-only --profile-kernel fp8|bf16
+                                                    (loop of the FP8 attention without the LSE,
+                                                     or of the BF16 attention with it)
        python bench.py --copy-only MIB              (plain device copy, counter calibration)
 """
 from __future__ import annotations
@@ -283,6 +286,9 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--profile-only", action="store_true",
                     help="run the step loop only (for rocprofv3), no JSON line")
+    ap.add_argument("--profile-kernel", choices=("step", "fp8", "bf16"), default="step",
+                    help="with --profile-only: loop the step, the FP8 attention without the "
+                         "LSE, or the BF16 attention with the LSE")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -332,6 +338,20 @@ def main() -> int:
         attn_fp8(True)
         b.record()
         ev_attn.append((a, b))
+
+    if args.profile_only and args.profile_kernel != "step":
+        if args.profile_kernel == "fp8":
+            quant()
+            one = lambda: attn_fp8(False)
+        else:
+            xb = {n: xd[n].to(torch.bfloat16) for n in "qkv"}
+            one = lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, lse,
+                                                  softmax_scale=w.softmax_scale)
+        for _ in range(args.warmup + args.steps):
+            one()
+        torch.cuda.synchronize()
+        log(f"bench: profile-only {args.profile_kernel} run done")
+        return 0
 
     log(f"bench: warmup {args.warmup} steps")
     for _ in range(args.warmup):

@@ -8,7 +8,10 @@ touches the GPU):
      `bench.py --copy-only 1024` (a plain 1 GiB device copy) to calibrate the two
      counters against a known byte count;
   3. --pmc passes of SQ/GRBM counters over the same command (matrix-pipe busy
-     cycles, VALU activity, LDS waits and bank conflicts, shader clock).
+     cycles, VALU activity, LDS waits and bank conflicts, shader clock);
+  4. steps 1 and 3 again for the FP8 kernel without the LSE (Lean P
+     probabilities, row sums on the matrix pipe) and the BF16 kernel with the
+     LSE, each looped alone by `bench.py --profile-only --profile-kernel`.
 It writes short text summaries plus traffic.json into OUTDIR (which is then
 copied into profiles/).  Raw rocprofv3 output stays in RAWDIR.
 
@@ -36,6 +39,13 @@ BENCH_KT = ["python", "bench.py", "--profile-only", "--steps", "20", "--warmup",
 BENCH = ["python", "bench.py", "--profile-only", "--steps", "3", "--warmup", "1"]
 COPY_MIB = 1024
 COPY = ["python", "bench.py", "--copy-only", str(COPY_MIB)]
+# the other two kernels of the metric: (tag, name pattern, profile-kernel choice, title)
+OTHERS = [
+    ("attn_fwd_fp8_d128_gauss32k", re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 0>"), "fp8",
+     "FP8 attention without the LSE (Lean P)"),
+    ("attn_fwd_bf16_d128_lse_gauss32k", re.compile(r"attn_fwd_kernel<false, 128, 64, 8, 1>"),
+     "bf16", "BF16 attention with the LSE"),
+]
 SQ_PASSES = [
     ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
      "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"],
@@ -78,6 +88,39 @@ def counters(d, match):
 def mean_over(vals, key):
     xs = [v[key] for v in vals.values() if key in v]
     return sum(xs) / len(xs)
+
+
+def sq_summary(prog, kre, raw, name, title, path):
+    """SQ/GRBM counter passes over `prog` for the kernels matching `kre`, summarised
+    (means per dispatch plus derived ratios) into `path`."""
+    agg, cmdl = {}, []
+    for i, p in enumerate(SQ_PASSES):
+        d, c = rocprof(["--pmc", *p], prog, raw, f"{name}{i}")
+        cmdl.append(c)
+        v, dur = counters(d, kre)
+        for k in p:
+            agg[k] = mean_over(v, k)
+        agg.setdefault("dur_ns", sum(dur.values()) / len(dur))
+    xcd, cus, simds = 8, 256, 4
+    gui = agg["GRBM_GUI_ACTIVE"] / xcd                     # cycles per XCD
+    sclk = gui / agg["dur_ns"] * 1e3
+    simd_cycles = gui * cus * simds
+    lines = [f"# SQ/GRBM counters, {title} (means per dispatch)"]
+    lines += [f"# command: {c}" for c in cmdl]
+    lines += [f"{k:32s} {v:16.0f}" for k, v in agg.items()]
+    lines += ["", "derived:",
+              f"  shader clock             {sclk:8.0f} MHz (GRBM_GUI_ACTIVE / {xcd} XCDs / duration)",
+              f"  MFMA pipe busy           {agg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:8.3f} "
+              f"of SIMD cycles",
+              f"  VALU co-issued with MFMA {agg['SQ_VALU_MFMA_COEXEC_CYCLES'] / agg['SQ_VALU_MFMA_BUSY_CYCLES']:8.3f} "
+              f"of MFMA-busy cycles",
+              f"  VALU instr per MFMA      {agg['SQ_INSTS_VALU'] / agg['SQ_INSTS_MFMA']:8.2f}",
+              f"  LDS instr per MFMA       {agg['SQ_INSTS_LDS'] / agg['SQ_INSTS_MFMA']:8.2f}",
+              f"  LDS bank-conflict cycles per LDS instr "
+              f"{agg['SQ_LDS_BANK_CONFLICT'] / agg['SQ_INSTS_LDS']:8.2f}",
+              f"  LDS wait / wave cycles   {agg['SQ_WAIT_INST_LDS'] / agg['SQ_WAVE_CYCLES']:8.3f}"]
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def main() -> int:
@@ -150,34 +193,34 @@ def main() -> int:
                 f"LSE written once) {alg/2**20:.1f} MiB\n")
 
     # 3. SQ / GRBM counters
-    agg, cmdl = {}, []
-    for i, p in enumerate(SQ_PASSES):
-        d, c = rocprof(["--pmc", *p], BENCH, raw, f"sq{i}")
-        cmdl.append(c)
-        v, dur = counters(d, KERNEL_RE)
-        for k in p:
-            agg[k] = mean_over(v, k)
-        agg.setdefault("dur_ns", sum(dur.values()) / len(dur))
-    xcd, cus, simds = 8, 256, 4
-    gui = agg["GRBM_GUI_ACTIVE"] / xcd                     # cycles per XCD
-    sclk = gui / agg["dur_ns"] * 1e3
-    simd_cycles = gui * cus * simds
-    lines = [f"# SQ/GRBM counters, {kernel_name}, gauss32k with LSE (means per dispatch)"]
-    lines += [f"# command: {c}" for c in cmdl]
-    lines += [f"{k:32s} {v:16.0f}" for k, v in agg.items()]
-    lines += ["", "derived:",
-              f"  shader clock             {sclk:8.0f} MHz (GRBM_GUI_ACTIVE / {xcd} XCDs / duration)",
-              f"  MFMA pipe busy           {agg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:8.3f} "
-              f"of SIMD cycles",
-              f"  VALU co-issued with MFMA {agg['SQ_VALU_MFMA_COEXEC_CYCLES'] / agg['SQ_VALU_MFMA_BUSY_CYCLES']:8.3f} "
-              f"of MFMA-busy cycles",
-              f"  VALU instr per MFMA      {agg['SQ_INSTS_VALU'] / agg['SQ_INSTS_MFMA']:8.2f}",
-              f"  LDS instr per MFMA       {agg['SQ_INSTS_LDS'] / agg['SQ_INSTS_MFMA']:8.2f}",
-              f"  LDS bank-conflict cycles per LDS instr "
-              f"{agg['SQ_LDS_BANK_CONFLICT'] / agg['SQ_INSTS_LDS']:8.2f}",
-              f"  LDS wait / wave cycles   {agg['SQ_WAIT_INST_LDS'] / agg['SQ_WAVE_CYCLES']:8.3f}"]
-    with open(os.path.join(out, f"{TAG}_counters.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+    sq_summary(BENCH, KERNEL_RE, raw, "sq", f"{kernel_name}, gauss32k with LSE",
+               os.path.join(out, f"{TAG}_counters.txt"))
+
+    # 4. the FP8 kernel without the LSE and the BF16 kernel with it
+    for tag, kre, choice, title in OTHERS:
+        prog_kt = BENCH_KT + ["--profile-kernel", choice]
+        prog = BENCH + ["--profile-kernel", choice]
+        d, cmd = rocprof(["--kernel-trace", "--stats"], prog_kt, raw, f"kt_{choice}")
+        with open(os.path.join(d, "run_kernel_stats.csv")) as f:
+            rows = list(csv.DictReader(f))
+        name, avg = None, None
+        for r in rows:
+            if kre.search(r["Name"]):
+                name, avg = r["Name"], float(r["AverageNs"])
+        lines = [f"# rocprofv3 kernel statistics: {title}, gauss32k (B=1 Hq=32 Hkv=8 N=32768 "
+                 f"d=128), the kernel looped alone", f"# command: {cmd}", "",
+                 f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+                 f"{'pct':>6s}"]
+        for r in rows:
+            lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} "
+                         f"{float(r['AverageNs'])/1e3:10.1f} {float(r['MinNs'])/1e3:10.1f} "
+                         f"{float(r['MaxNs'])/1e3:10.1f} {float(r['Percentage']):6.2f}")
+        if avg:
+            lines += ["", f"kernel average {avg/1e3:.1f} us -> {flops / avg / 1e3:.1f} TFLOP/s"]
+        with open(os.path.join(out, f"{tag}_kernel_stats.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        sq_summary(prog, kre, raw, f"sq_{choice}", f"{name}, gauss32k ({title})",
+                   os.path.join(out, f"{tag}_counters.txt"))
     print("profile summaries written to", out, flush=True)
     return 0
 

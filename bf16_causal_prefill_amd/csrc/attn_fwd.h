@@ -392,18 +392,19 @@ void attn_fwd_kernel(FwdParams p) {
   auto block_exp = [&](float bmx, float nmc) -> float {
     return fminf(floorf(8.f - fmaf(bmx, c, nmc)), 127.f);
   };
-  // Exact probabilities of the 8 words of block nb (4 scores each), scaled by the block
-  // exponent (off = nmc + kb), rounded to e4m3 into pf8[nb]; bs[j] receives the sum of
-  // the j-th scores of the words (four independent chains, started from the first word
-  // rather than from zero, which would cost an add of 0 per chain).
-  auto exact_words = [&](int nb, float off, float* bs) {
+  // The 8 words of block nb (4 probabilities each, already exponentiated in place of
+  // the scores and scaled by the block exponent) rounded to e4m3 into pf8[nb]; bs[j]
+  // receives the sum of the j-th probabilities of the words (four independent chains,
+  // started from the first word rather than from zero, which would cost an add of 0 per
+  // chain).
+  auto exact_words = [&](int nb, float* bs) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = 4 * w + j;
-        pv[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * nb + (e >> 4)][e & 15], c, off));
+        pv[j] = s[2 * nb + (e >> 4)][e & 15];
         bs[j] = w == 0 ? pv[j] : bs[j] + pv[j];
       }
       // high half first into the word being replaced, so no zeroed register
@@ -543,42 +544,85 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const float nmc = -m_run * c;
 
-    if constexpr (FP8) {
+    if constexpr (EXACT) {
+      // Exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact fp32
+      // sum (scale removed) normalises O and gives the log-sum-exp.  Staged like the
+      // Lean P words below: all exponent arguments, then all exponentials (in place of
+      // the scores), then the words and the sums.
+      float kbf[C::NB];
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        // one block exponent per query and 64-key block (both operand scale blocks)
+        kbf[nb] = block_exp(bmx[nb], nmc);
+        psc[nb] = 127 - (int)kbf[nb];
+        const float off = nmc + kbf[nb];
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          s[2 * nb + (e >> 4)][e & 15] = fmaf(s[2 * nb + (e >> 4)][e & 15], c, off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          s[2 * nb + (e >> 4)][e & 15] = __builtin_amdgcn_exp2f(s[2 * nb + (e >> 4)][e & 15]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        float bs[4];
+        exact_words(nb, bs);
+        lx_run += __builtin_ldexpf((bs[0] + bs[1]) + (bs[2] + bs[3]), -(int)kbf[nb]);
+      }
+    } else if constexpr (FP8) {
+      // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each.  All
+      // code arguments are formed first (in place of the scores), then the words are
+      // packed a byte position at a time across all of them, so that no instruction
+      // waits on the one just before it (+1% against packing one word at a time).
       const float A = 8.f * c;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
         // one block exponent per query and 64-key block (both operand scale blocks)
         const float kbf = block_exp(bmx[nb], nmc);
         psc[nb] = 127 - (int)kbf;
-        if constexpr (EXACT) {
-          // exact probabilities scaled by 2^kb (<= 2^8), rounded to e4m3; their exact
-          // fp32 sum (scale removed) normalises O and gives the log-sum-exp
-          const float off = nmc + kbf;
-          float bs[4];
-          exact_words(nb, off, bs);
-          lx_run += __builtin_ldexpf((bs[0] + bs[1]) + (bs[2] + bs[3]), -(int)kbf);
-        } else {
-          // Lean P: e4m3 code = integer conversion of 8 (x + kb) + C0, one FMA each
-          const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
+        const float Bc = fmaf(8.f, kbf, fmaf(8.f, nmc, LEANP_C0));
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          s[2 * nb + (e >> 4)][e & 15] = fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc);
+      }
+      uint32_t words[C::NB][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
-            uint32_t word = 0u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 4 * w + j;
-              word = __builtin_amdgcn_cvt_pk_u8_f32(
-                  fmaf(s[2 * nb + (e >> 4)][e & 15], A, Bc), j, word);
-            }
-            pf8[nb][w] = (int)word;
+            const int e = 4 * w + j;
+            words[nb][w] = __builtin_amdgcn_cvt_pk_u8_f32(s[2 * nb + (e >> 4)][e & 15], j,
+                                                          j == 0 ? 0u : words[nb][w]);
           }
-        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pf8[nb][w] = (int)words[nb][w];
     } else {
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};     // independent partial sums
+      // staged: all exponent arguments, then all exponentials (in place of the
+      // scores), then the bf16 operands and the sums (four independent chains, each
+      // started from its first probability)
+#pragma unroll
+      for (int e = 0; e < 16 * C::MT; ++e) s[e >> 4][e & 15] = fmaf(s[e >> 4][e & 15], c, nmc);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 16 * C::MT; ++e)
+        s[e >> 4][e & 15] = __builtin_amdgcn_exp2f(s[e >> 4][e & 15]);
+      __builtin_amdgcn_sched_barrier(0);
+      float rs[4];
 #pragma unroll
       for (int e = 0; e < 16 * C::MT; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c, nmc));
-        rs[e & 3] += pv;
+        const float pv = s[e >> 4][e & 15];
+        rs[e & 3] = e < 4 ? pv : rs[e & 3] + pv;
         pfb[e >> 3][e & 7] = (__bf16)pv;
       }
       l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);

@@ -1,0 +1,203 @@
+"""GPU edge cases against the fp64 oracle, through the C ABI.
+
+* quantize_e4m3 on degenerate tensors: all zeros (descale 1), one all-zero head in
+  per-head mode, exact rounding ties between neighbouring e4m3 values, signed zeros
+  and values below half the smallest subnormal: bit-exact codes and descales.
+* Extreme score patterns: scores that rise along the key axis by more than the lazy
+  rescale threshold in every key tile (the running max moves on every tile), and
+  scores that fall so steeply that most probabilities underflow (rows dominated by
+  their first keys, block exponents at their cap, probabilities flushed to zero).
+* The largest launch the entry points accept: B*N*Hq*d one batch short of 2^31
+  elements (they reject 2^31 and above), inputs drawn on the device, outputs
+  compared on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import DEV, bf16_bytes, check, gpu_quantize, note, run_bf16, run_fp8
+
+import bf16_causal_prefill_amd as ba
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- quantize_e4m3 on degenerate inputs ------------------------------------------------
+
+def _e4m3_grid() -> np.ndarray:
+    """Every finite non-negative e4m3 value, the midpoints between neighbours (exact
+    in float32; round-to-nearest-even ties), values just off each midpoint, and values
+    at and below half the smallest subnormal 2^-9."""
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    down = np.nextafter(mids, np.float32(0))
+    tiny = np.array([2.0 ** -10, 2.0 ** -11, 1e-30, 1e-40, 0.0], np.float32)
+    g = np.concatenate([vals, mids, up, down, tiny]).astype(np.float32)
+    return np.concatenate([g, -g])
+
+
+QZ_CASES = ["zeros_tensor", "zeros_one_head", "ties_tensor", "ties_head"]
+
+
+@pytest.mark.parametrize("case", QZ_CASES)
+def test_quantize_degenerate(case):
+    note(f"case quantize {case}")
+    rng = np.random.default_rng(41)
+    if case == "zeros_tensor":
+        x, per_head = np.zeros((2, 33, 3, 128), np.float32), False
+    elif case == "zeros_one_head":
+        x, per_head = rng.standard_normal((1, 70, 4, 128)).astype(np.float32), True
+        x[:, :, 2, :] = 0.0
+    else:
+        g = _e4m3_grid()
+        # 2 * 1024 grid slots; absmax is exactly 448 in every head, so the descale is
+        # exactly 1 and the quotients are the grid values themselves
+        n = 2 * 8 * 128
+        x = np.resize(g, n).reshape(1, 2, 8, 128).astype(np.float32)
+        x[0, 0, :, 0] = 448.0
+        x = np.concatenate([x, x[:, :, ::-1, ::-1]], axis=1)   # (1, 4, 8, 128)
+        per_head = case == "ties_head"
+    codes_d, ds_d = gpu_quantize(x, per_head)
+    codes_h, ds_h = oracle.quantize_e4m3(x, per_head)
+    assert np.array_equal(ds_d.cpu().numpy().view(np.uint32), ds_h.view(np.uint32))
+    assert np.array_equal(codes_d.cpu().numpy(), codes_h)
+    if case.startswith("zeros"):
+        zero_heads = [0, 1, 2] if case == "zeros_tensor" else [2]
+        for h in zero_heads:
+            assert np.all(codes_h[:, :, h, :] == 0)
+        assert ds_h[zero_heads[-1] if per_head else 0] == 1.0
+    else:
+        assert np.all(ds_h == 1.0)
+
+
+# ---- extreme score patterns ------------------------------------------------------------
+
+def _slope_inputs(N: int, slope_log2: float, seed: int):
+    """Q = a e_0 for every query, K_j = b_j e_0, V ~ N(0, 1): the score of key j is
+    (linear in j) so that, in log2 units after the softmax scale, it changes by
+    slope_log2 per key.  One nonzero channel keeps every score an exact product."""
+    B, Hq, Hkv, d = 1, 4, 2, 128
+    scale = 1.0 / np.sqrt(d)
+    c = scale * np.log2(np.e)
+    a = 16.0
+    rng = np.random.default_rng(seed)
+    q = np.zeros((B, N, Hq, d), np.float32)
+    k = np.zeros((B, N, Hkv, d), np.float32)
+    q[..., 0] = a
+    k[..., 0] = (slope_log2 / (c * a) * np.arange(N, dtype=np.float64))[None, :, None]
+    v = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    return {"q": q, "k": k, "v": v}, scale
+
+
+SLOPES = {"rising": 0.1, "falling": -0.75}
+
+
+@pytest.mark.parametrize("pattern", list(SLOPES))
+@pytest.mark.parametrize("prec", ["bf16", "fp8", "fp8_nolse"])
+def test_extreme_score_slopes(pattern, prec):
+    """rising: the row max grows by 12.8 (log2) per 128-key tile, above the rescale
+    threshold of 8, so every tile rescales; falling: scores drop by 96 per tile, so
+    from the second tile on every probability underflows.  fp8_nolse is the FP8 call
+    without the LSE (the linear-code probabilities and their row sums)."""
+    N = 1000
+    x, scale = _slope_inputs(N, SLOPES[pattern], seed=43)
+    note(f"case slope {pattern} {prec}: N={N}")
+    if prec == "bf16":
+        qu, ku, vu = (bf16_bytes(x[n]) for n in "qkv")
+        q, k, v = (oracle.bf16_decode(a) for a in (qu, ku, vu))
+        out = run_bf16(qu, ku, vu, scale)[0]
+    else:
+        dev, host = [], []
+        for n in "qkv":
+            cd, dd = gpu_quantize(x[n], False)
+            ch, dh = oracle.quantize_e4m3(x[n], False)
+            assert np.array_equal(cd.cpu().numpy(), ch)
+            dev.append((cd, dd))
+            host.append(oracle.e4m3_decode(ch) * float(dh[0]))
+        q, k, v = host
+        (qc, qd), (kc, kd), (vc, vd) = dev
+        out = run_fp8(qc, kc, vc, qd, kd, vd, False, scale, want_lse=prec == "fp8")[0]
+    ro, rl = oracle.causal_attention(q, k, v, scale)
+    if prec == "fp8_nolse":
+        check(f"slope_{pattern}", "fp8", out.o, ro)
+    else:
+        check(f"slope_{pattern}", prec, out.o, ro, out.lse, rl)
+
+
+# ---- the largest accepted launch ---------------------------------------------------------
+
+# B*N*Hq*d = 1023 * 512 * 32 * 128 = 2^31 - 2^21 elements per Q / O tensor (the entry
+# points reject 2^31 and above); 65472 workgroups.
+MAX_SHAPE = dict(B=1023, N=512, Hq=32, Hkv=8, d=128)
+
+
+def _max_rows(rng):
+    B, N, Hq = MAX_SHAPE["B"], MAX_SHAPE["N"], MAX_SHAPE["Hq"]
+    rows = [(b, h, i) for b in (0, B // 2, B - 1) for h in (0, Hq - 1) for i in (0, 255, 256, N - 1)]
+    rows += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(N))) for _ in range(24)]
+    return rows
+
+
+def _oracle_rows_from_device(tensors, decoders, scale, rows):
+    """Oracle rows from per-batch slices copied off the device (the oracle never sees
+    the whole multi-GiB tensors); decoders map a device slice to float64 values."""
+    q, k, v = tensors
+    ro = np.empty((len(rows), v.shape[3]))
+    rl = np.empty(len(rows))
+    by_b = {}
+    for r, (b, h, i) in enumerate(rows):
+        by_b.setdefault(b, []).append(r)
+    for b, idx in by_b.items():
+        qb, kb, vb = (dec(t[b:b + 1]) for dec, t in zip(decoders, tensors))
+        o1, l1 = oracle.causal_attention_rows(qb, kb, vb, scale,
+                                              [(0, rows[r][1], rows[r][2]) for r in idx])
+        ro[idx], rl[idx] = o1, l1
+    return ro, rl
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp8"])
+def test_largest_launch_sampled_rows(prec):
+    B, N, Hq, Hkv, d = (MAX_SHAPE[k] for k in ("B", "N", "Hq", "Hkv", "d"))
+    assert B * N * Hq * d < 2 ** 31 <= (B + 1) * N * Hq * d
+    note(f"case largest launch {prec}: B={B} N={N} Hq={Hq} Hkv={Hkv} d={d}")
+    scale = 1.0 / np.sqrt(d)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(47)
+    dt = torch.bfloat16 if prec == "bf16" else torch.float8_e4m3fn
+
+    def draw(H):   # N(0, 1) drawn per batch on the device, stored in the kernel's dtype
+        t = torch.empty((B, N, H, d), device=DEV, dtype=dt)
+        for b in range(B):
+            t[b] = torch.randn((N, H, d), device=DEV, generator=gen).to(dt)
+        return t
+
+    q, k, v = draw(Hq), draw(Hkv), draw(Hkv)
+    o = torch.full((B, N, Hq, d), float("nan"), device=DEV, dtype=torch.bfloat16)
+    lse = torch.full((B, Hq, N), float("nan"), device=DEV, dtype=torch.float32)
+    if prec == "bf16":
+        ba.attn_fwd_causal_bf16(q, k, v, o, lse, softmax_scale=scale)
+        tensors = (q, k, v)
+        dec = lambda t: oracle.bf16_decode(t.view(torch.int16).cpu().numpy().view(np.uint16))
+        decoders = (dec, dec, dec)
+    else:
+        # per-tensor descales 1/2 (q), 1 (k) and 2 (v) on the drawn codes
+        descales = (0.5, 1.0, 2.0)
+        tensors = tuple(t.view(torch.uint8) for t in (q, k, v))
+        dq, dk, dv = (torch.full((1,), s, device=DEV) for s in descales)
+        ba.attn_fwd_causal_fp8(*tensors, dq, dk, dv, o, lse, softmax_scale=scale,
+                               descale_per_head=0)
+        decoders = tuple((lambda t, s=s: oracle.e4m3_decode(t.cpu().numpy()) * s)
+                         for s in descales)
+    torch.cuda.synchronize()
+    rows = _max_rows(np.random.default_rng(49))
+    ro, rl = _oracle_rows_from_device(tensors, decoders, scale, rows)
+    bb = torch.tensor([r[0] for r in rows], device=DEV)
+    hh = torch.tensor([r[1] for r in rows], device=DEV)
+    ii = torch.tensor([r[2] for r in rows], device=DEV)
+    go = o[bb, ii, hh].float().cpu().numpy().astype(np.float64)
+    gl = lse[bb, hh, ii].cpu().numpy().astype(np.float64)
+    # every output element was written (the buffers started as NaN)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    check("largest_launch/rows", prec, go, ro, gl, rl)

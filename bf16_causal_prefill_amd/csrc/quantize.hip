@@ -44,6 +44,13 @@ constexpr int QZ_U = 4;
 // in the band, so each column's head is fixed per thread and the workgroup reads whole
 // rows (contiguous memory) at a time, QZ_U rows in flight per thread.
 
+// Non-temporal 16-byte load: the float32 input is streamed through once per pass.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 __global__ void qz_clear(uint32_t* amax_bits, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) amax_bits[i] = 0u;
@@ -131,13 +138,13 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict_
     for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
       float4 a[QZ_U];
 #pragma unroll
-      for (int u = 0; u < QZ_U; ++u) a[u] = col[(size_t)u * L4];
+      for (int u = 0; u < QZ_U; ++u) a[u] = load_stream(col + (size_t)u * L4);
       col += (size_t)QZ_U * L4;
 #pragma unroll
       for (int u = 0; u < QZ_U; ++u) m[u] = fmaxf(m[u], absmax4(wht_block<HB4>(a[u], lane)));
     }
     for (; r < r1; ++r) {
-      m[0] = fmaxf(m[0], absmax4(wht_block<HB4>(col[0], lane)));
+      m[0] = fmaxf(m[0], absmax4(wht_block<HB4>(load_stream(col), lane)));
       col += L4;
     }
     float mm = m[0];
@@ -205,14 +212,14 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
       float4 a[QZ_U];
 #pragma unroll
-      for (int u = 0; u < QZ_U; ++u) a[u] = src[(size_t)u * L4];
+      for (int u = 0; u < QZ_U; ++u) a[u] = load_stream(src + (size_t)u * L4);
       src += (size_t)QZ_U * L4;
 #pragma unroll
       for (int u = 0; u < QZ_U; ++u) dst[(size_t)u * L4] = e4m3_word(wht_block<HB4>(a[u], lane), ds);
       dst += (size_t)QZ_U * L4;
     }
     for (; r < r1; ++r) {
-      dst[0] = e4m3_word(wht_block<HB4>(src[0], lane), ds);
+      dst[0] = e4m3_word(wht_block<HB4>(load_stream(src), lane), ds);
       src += L4;
       dst += L4;
     }

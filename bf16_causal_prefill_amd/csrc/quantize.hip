@@ -34,7 +34,8 @@ namespace attn {
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_LDS_HEADS = 1024;   // per-head maxima kept in LDS up to this many heads
 // Workgroups per pass (about four per CU) and rows in flight per thread: measured best
-// of 1024/2048/4096 workgroups and 2/4/8 rows on the 16K-32K-row tensors.
+// of 512/768/1024/2048/4096 workgroups and 2/4/8 rows on the 16K-32K-row tensors (with
+// the non-temporal loads as well).
 constexpr int QZ_TARGET_WGS = 1024;
 constexpr int QZ_U = 4;
 

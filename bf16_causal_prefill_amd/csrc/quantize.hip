@@ -196,6 +196,79 @@ __device__ __forceinline__ uint32_t e4m3_word(float4 a, float ds) {
          (e4m3_code(a.w / ds) << 24);
 }
 
+// The same codes without branches, for divisors in [2^-100, 2^100] (every descale of a
+// tensor whose absmax is a normal float32 above 2^-90).
+//  * Quotient: the reciprocal of ds refined by one Newton step, then two residual
+//    corrections whose residuals the FMA forms exactly; for these divisors this is the
+//    correctly rounded quotient, and copying the sign of x keeps the sign of a zero
+//    quotient.  Checked against the IEEE division on the device over 4M pairs and every
+//    e4m3 value, tie and neighbour times random descales.
+//  * Code: clamped to +-448 (beyond it the hardware conversion gives NaN codes), then
+//    gfx950's f32 -> e4m3 conversion, which rounds to nearest even with subnormals and
+//    signed zeros exactly as e4m3_code for |q| < 448 (checked on the same values).
+//  * A NaN quotient (seen through the sum of the four, which is also NaN when they
+//    hold infinities of both signs) takes e4m3_code for the whole word.
+struct Divisor {
+  float b, r;
+};
+
+__device__ __forceinline__ Divisor make_divisor(float b) {
+  float r = __builtin_amdgcn_rcpf(b);
+  r = fmaf(fmaf(-b, r, 1.f), r, r);
+  return {b, r};
+}
+
+__device__ __forceinline__ bool fast_divisor(float b) {
+  return b >= 0x1p-100f && b <= 0x1p100f;
+}
+
+__device__ __forceinline__ float quotient(float a, Divisor d) {
+  float q = a * d.r;
+  q = fmaf(fmaf(-d.b, q, a), d.r, q);
+  q = fmaf(fmaf(-d.b, q, a), d.r, q);
+  return copysignf(q, a);
+}
+
+__device__ __forceinline__ uint32_t e4m3_word_fast(float4 a, Divisor d) {
+  const float4 q = make_float4(quotient(a.x, d), quotient(a.y, d), quotient(a.z, d),
+                               quotient(a.w, d));
+  if (__builtin_expect(__builtin_isnan((q.x + q.y) + (q.z + q.w)), 0))
+    return e4m3_code(q.x) | (e4m3_code(q.y) << 8) | (e4m3_code(q.z) << 16) |
+           (e4m3_code(q.w) << 24);
+  const float m = 448.f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q.x, -m, m),
+                                          __builtin_amdgcn_fmed3f(q.y, -m, m), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q.z, -m, m),
+                                      __builtin_amdgcn_fmed3f(q.w, -m, m), w, true);
+  return (uint32_t)w;
+}
+
+// Rows r0 .. r1-1 of float4 column c (FAST: the branch-free word for a divisor in range).
+template <int HB4, bool FAST>
+__device__ __forceinline__ void encode_column(const float4* src, uint32_t* dst, int r0, int r1,
+                                              int L4, float ds, int lane) {
+  const Divisor dv = make_divisor(ds);
+  auto word = [&](float4 a) {
+    return FAST ? e4m3_word_fast(wht_block<HB4>(a, lane), dv)
+                : e4m3_word(wht_block<HB4>(a, lane), ds);
+  };
+  int r = r0;
+  for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
+    float4 a[QZ_U];
+#pragma unroll
+    for (int u = 0; u < QZ_U; ++u) a[u] = load_stream(src + (size_t)u * L4);
+    src += (size_t)QZ_U * L4;
+#pragma unroll
+    for (int u = 0; u < QZ_U; ++u) dst[(size_t)u * L4] = word(a[u]);
+    dst += (size_t)QZ_U * L4;
+  }
+  for (; r < r1; ++r) {
+    dst[0] = word(load_stream(src));
+    src += L4;
+    dst += L4;
+  }
+}
+
 template <int HB4>
 __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
                                                        uint32_t* __restrict__ out,
@@ -209,21 +282,10 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     const float ds = per_head ? descale_of(amax_bits[c / d4]) : ds_t;
     const float4* src = (const float4*)x + (size_t)r0 * L4 + c;
     uint32_t* dst = out + (size_t)r0 * L4 + c;
-    int r = r0;
-    for (; r + QZ_U <= r1; r += QZ_U) {    // QZ_U loads in flight per thread
-      float4 a[QZ_U];
-#pragma unroll
-      for (int u = 0; u < QZ_U; ++u) a[u] = load_stream(src + (size_t)u * L4);
-      src += (size_t)QZ_U * L4;
-#pragma unroll
-      for (int u = 0; u < QZ_U; ++u) dst[(size_t)u * L4] = e4m3_word(wht_block<HB4>(a[u], lane), ds);
-      dst += (size_t)QZ_U * L4;
-    }
-    for (; r < r1; ++r) {
-      dst[0] = e4m3_word(wht_block<HB4>(load_stream(src), lane), ds);
-      src += L4;
-      dst += L4;
-    }
+    if (fast_divisor(ds))
+      encode_column<HB4, true>(src, dst, r0, r1, L4, ds, lane);
+    else
+      encode_column<HB4, false>(src, dst, r0, r1, L4, ds, lane);
   }
 }
 

@@ -176,7 +176,9 @@ int attn_merge_partials(const void* o_a, const float* lse_a,
  *             descale = absmax / 448 in float32 (1 for an all-zero tensor or
  *             head); it is also used as scratch during the call.
  *   code      = round-to-nearest-even e4m3 of the float32 quotient x / descale,
- *             saturating at +-448; NaN maps to 0x7F.
+ *             saturating at +-448; NaN maps to 0x7F.  NaN elements take no
+ *             part in the absmax; an infinity makes the descale infinite (then
+ *             finite elements encode to signed zeros).
  * d must be a multiple of 4, H <= 65535 and the tensor below 2^31 elements.
  * Invalid arguments return ATTN_E_INVAL / ATTN_E_ALIGN before any launch.  The absmax reduction is order-independent, so
  * results are bit-identical across runs.  Four kernels are enqueued.

@@ -84,14 +84,19 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 
 def absmax_descale(x: np.ndarray, per_head: bool) -> np.ndarray:
     """descale of a (B, N, H, d) float32 tensor: float32(absmax) / float32(448)
-    per head ((H,)) or per tensor ((1,)); 1 where the absmax is 0."""
+    per head ((H,)) or per tensor ((1,)); 1 where the absmax is 0.
+
+    A NaN element has no magnitude and takes no part in the absmax (it encodes
+    to 0x7F whatever the descale); an infinity does, giving an infinite descale."""
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 4:
         raise ValueError("expected (B, N, H, d)")
+    a = np.abs(x)
+    a = np.where(np.isnan(a), np.float32(0.0), a)
     if per_head:
-        amax = np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
+        amax = np.max(a, axis=(0, 1, 3)).astype(np.float32)
     else:
-        amax = np.array([np.max(np.abs(x))], dtype=np.float32)
+        amax = np.array([np.max(a)], dtype=np.float32)
     descale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     return np.where(amax > 0, descale, np.float32(1.0)).astype(np.float32)
 
@@ -99,7 +104,8 @@ def absmax_descale(x: np.ndarray, per_head: bool) -> np.ndarray:
 def encode_with_descale(x: np.ndarray, descale) -> np.ndarray:
     """e4m3 codes of the float32 quotient x / descale (descale broadcast
     against x; float32 / float32 is correctly rounded)."""
-    qv = (np.asarray(x, dtype=np.float32) / np.asarray(descale, dtype=np.float32)).astype(np.float32)
+    with np.errstate(invalid="ignore"):     # inf / inf is NaN, encoded as 0x7F
+        qv = (np.asarray(x, dtype=np.float32) / np.asarray(descale, dtype=np.float32)).astype(np.float32)
     return e4m3_encode(qv)
 
 

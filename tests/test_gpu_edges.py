@@ -2,7 +2,8 @@
 
 * quantize_e4m3 on degenerate tensors: all zeros (descale 1), one all-zero head in
   per-head mode, exact rounding ties between neighbouring e4m3 values, signed zeros
-  and values below half the smallest subnormal: bit-exact codes and descales.
+  and values below half the smallest subnormal, NaN elements (no part in the absmax,
+  code 0x7F) and an infinity (infinite descale): bit-exact codes and descales.
 * Extreme score patterns: scores that rise along the key axis by more than the lazy
   rescale threshold in every key tile (the running max moves on every tile), and
   scores that fall so steeply that most probabilities underflow (rows dominated by
@@ -38,7 +39,8 @@ def _e4m3_grid() -> np.ndarray:
     return np.concatenate([g, -g])
 
 
-QZ_CASES = ["zeros_tensor", "zeros_one_head", "ties_tensor", "ties_head"]
+QZ_CASES = ["zeros_tensor", "zeros_one_head", "ties_tensor", "ties_head", "nan_tensor",
+            "nan_head", "inf_tensor", "inf_head"]
 
 
 @pytest.mark.parametrize("case", QZ_CASES)
@@ -50,7 +52,7 @@ def test_quantize_degenerate(case):
     elif case == "zeros_one_head":
         x, per_head = rng.standard_normal((1, 70, 4, 128)).astype(np.float32), True
         x[:, :, 2, :] = 0.0
-    else:
+    elif case.startswith("ties"):
         g = _e4m3_grid()
         # 2 * 1024 grid slots; absmax is exactly 448 in every head, so the descale is
         # exactly 1 and the quotients are the grid values themselves
@@ -59,6 +61,22 @@ def test_quantize_degenerate(case):
         x[0, 0, :, 0] = 448.0
         x = np.concatenate([x, x[:, :, ::-1, ::-1]], axis=1)   # (1, 4, 8, 128)
         per_head = case == "ties_head"
+    elif case.startswith("nan"):
+        # NaN elements leave the absmax as if absent and encode to 0x7F; in per-head
+        # mode head 3 holds nothing but NaN (descale 1)
+        x = rng.standard_normal((2, 40, 4, 128)).astype(np.float32)
+        x[0, 5, 1, 7] = np.nan
+        x[1, 39, 0, 127] = -np.nan
+        x[:, :, 3, :] = np.nan
+        per_head = case == "nan_head"
+    elif case.startswith("inf"):
+        # an infinity makes the descale infinite: finite elements encode to signed
+        # zeros, the infinity itself (inf / inf) to 0x7F
+        x = rng.standard_normal((1, 40, 4, 128)).astype(np.float32)
+        x[0, 11, 2, 64] = -np.inf
+        per_head = case == "inf_head"
+    else:
+        raise ValueError(case)
     codes_d, ds_d = gpu_quantize(x, per_head)
     codes_h, ds_h = oracle.quantize_e4m3(x, per_head)
     assert np.array_equal(ds_d.cpu().numpy().view(np.uint32), ds_h.view(np.uint32))
@@ -68,8 +86,13 @@ def test_quantize_degenerate(case):
         for h in zero_heads:
             assert np.all(codes_h[:, :, h, :] == 0)
         assert ds_h[zero_heads[-1] if per_head else 0] == 1.0
-    else:
+    elif case.startswith("ties"):
         assert np.all(ds_h == 1.0)
+    elif case.startswith("nan"):
+        assert np.all(codes_h[np.isnan(x)] == 0x7F)
+        assert np.all(np.isfinite(ds_h)) and (not per_head or ds_h[3] == 1.0)
+    else:
+        assert np.isinf(ds_h[2 if per_head else 0])
 
 
 # ---- extreme score patterns ------------------------------------------------------------

@@ -123,6 +123,37 @@ def test_quantize_error_bound_and_zero_tensor():
     assert np.all(zc == 0) and np.all(zd == 1.0)
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_nan_and_inf_elements(per_head):
+    """Reading: a NaN has no magnitude, so it leaves the absmax (and every other code)
+    as if it were absent and encodes to 0x7F; an infinity sets an infinite descale, so
+    every finite element encodes to a signed zero and the infinity (inf/inf) to 0x7F."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((1, 16, 3, 8)).astype(np.float32)
+    y = x.copy()
+    y[0, 3, 0, 1] = np.nan
+    y[0, 7, 1, 5] = -np.nan
+    y[0, :, 2, :] = np.nan                        # a head with no magnitude at all
+    cy, dy = oracle.quantize_e4m3(y, per_head)
+    nan = np.isnan(y)
+    assert np.all(cy[nan] == 0x7F)
+    x0 = np.where(nan, np.float32(0.0), y)
+    c0, d0 = oracle.quantize_e4m3(x0, per_head)
+    assert np.array_equal(dy.view(np.uint32), d0.view(np.uint32))
+    assert np.array_equal(cy[~nan], c0[~nan])
+    if per_head:
+        assert dy[2] == 1.0 and dy[0] == np.float32(np.max(np.abs(x[:, :, 0]))) / np.float32(448)
+    z = x.copy()
+    z[0, 2, 1, 3] = np.inf
+    cz, dz = oracle.quantize_e4m3(z, per_head)
+    assert np.isinf(dz[1 if per_head else 0])
+    assert cz[0, 2, 1, 3] == 0x7F
+    sl = (slice(None), slice(None), 1) if per_head else (Ellipsis,)
+    finite = np.isfinite(z[sl])
+    assert np.all((cz[sl][finite] & 0x7F) == 0)
+    assert np.array_equal(cz[sl][finite] >> 7, np.signbit(z[sl][finite]).astype(np.uint8))
+
+
 # ---- Hadamard rotation before quantisation ----------------------------------------
 
 def _sylvester(n):

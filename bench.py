@@ -2,7 +2,8 @@
 
 One step = the whole FP8 path over one batch of the "gauss32k" workload
 (B=1, Hq=32, Hkv=8, N=32768, d=128, iid N(0,1) inputs already resident in HBM
-as float32): quantize_e4m3 of Q, K and V (per-tensor scales), then
+as float32): quantize_e4m3 of K and V (per-tensor scales) and quantize_e4m3_q_pow2
+of Q (the per-tensor scale that makes the FP8 softmax constant a power of two), then
 attn_fwd_causal_fp8 writing O (bf16) and the LSE (fp32).  `value` is the causal
 TFLOP/s of that step, counting only the attention FLOPs 4*B*Hq*N^2*d/2.
 
@@ -196,8 +197,13 @@ def cpu_baseline(w, x, n_heads: int):
     G = w.Hq // w.Hkv
     n_kv = (n_heads + G - 1) // G
     dec = {}
-    for n, hs in (("q", n_heads), ("k", n_kv), ("v", n_kv)):
+    dsk = oracle.absmax_descale(x["k"], per_head=False)
+    for n, hs in (("k", n_kv), ("v", n_kv), ("q", n_heads)):
         ds = oracle.absmax_descale(x[n], per_head=False)
+        if n == "q":      # the Q descale of quantize_e4m3_q_pow2, from the whole tensor
+            amax = np.float32(np.max(np.abs(x[n])))
+            ds = np.array([oracle.pow2_q_descale_one(amax, dsk[0], w.softmax_scale)],
+                          np.float32)
         codes = oracle.encode_with_descale(x[n][:, :, :hs], ds[0])
         dec[n] = oracle.e4m3_decode(codes) * float(ds[0])
     t0 = time.perf_counter()
@@ -320,8 +326,12 @@ def main() -> int:
     flops = workloads.causal_flops(w)
 
     def quant():
-        for n in "qkv":
+        # K and V with their absmax scales, then Q with the scale that makes the FP8
+        # softmax constant a power of two (given K's descales)
+        for n in "kv":
             ba.quantize_e4m3(xd[n], codes[n], ds[n], per_head=w.fp8_per_head)
+        ba.quantize_e4m3_q_pow2(xd["q"], codes["q"], ds["q"], ds["k"], w.softmax_scale,
+                                per_head=w.fp8_per_head)
 
     def attn_fp8(with_lse=True):
         ba.attn_fwd_causal_fp8(codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"],
@@ -389,6 +399,15 @@ def main() -> int:
             codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], o, lse, q_offset=0,
             softmax_scale=w.softmax_scale, descale_per_head=int(w.fp8_per_head)), 10)
         extra["fp8_attn_rounded_lse_tflops"] = round(flops / t / 1e9, 1)
+        # the FP8 attention with the LSE on Q quantised with its plain absmax scale (the
+        # softmax constant then takes one multiply-add per score)
+        qa, da = torch.empty_like(codes["q"]), torch.empty_like(ds["q"])
+        ba.quantize_e4m3(xd["q"], qa, da, per_head=w.fp8_per_head)
+        t = time_events(lambda: ba.attn_fwd_causal_fp8(
+            qa, codes["k"], codes["v"], da, ds["k"], ds["v"], o, lse,
+            softmax_scale=w.softmax_scale, descale_per_head=int(w.fp8_per_head)), 10)
+        extra["fp8_attn_lse_absmax_q_tflops"] = round(flops / t / 1e9, 1)
+        del qa, da
         t = time_events(quant, 10)
         qbytes = sum(x[n].nbytes * 2 + x[n].size for n in "qkv")   # 2 reads + code write
         extra["quantize_qkv_ms"] = round(t, 4)
@@ -426,8 +445,10 @@ def main() -> int:
         fm = workloads.causal_flops(wm)
         cm = {n: torch.empty(xm[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
         dm = {n: torch.empty(xm[n].shape[2], device=dev) for n in "qkv"}
-        for n in "qkv":
+        for n in "kv":
             ba.quantize_e4m3(xmd[n], cm[n], dm[n], per_head=True)
+        ba.quantize_e4m3_q_pow2(xmd["q"], cm["q"], dm["q"], dm["k"], wm.softmax_scale,
+                                per_head=True)
         for tag, L in (("mla32k_fp8_attn_lse", lm), ("mla32k_fp8_attn_nolse", None)):
             t = time_events(lambda: ba.attn_fwd_causal_fp8(
                 cm["q"], cm["k"], cm["v"], dm["q"], dm["k"], dm["v"], om, L,
@@ -461,7 +482,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
                    "d_qk": w.d_qk, "d_v": w.d_v, "inputs": "iid N(0,1) float32 in HBM",
-                   "step": "quantize_e4m3(q,k,v) per tensor + attn_fwd_causal_fp8 (O + LSE)"},
+                   "step": "quantize_e4m3(k,v) + quantize_e4m3_q_pow2(q), per tensor, "
+                            "+ attn_fwd_causal_fp8 (O + LSE)"},
         "pct_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<fp8, d128> (with LSE)",
                      "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],

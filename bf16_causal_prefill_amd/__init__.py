@@ -16,7 +16,8 @@ import os
 __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
            "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
            "attn_fwd_causal_offset_fp8_rounded_lse", "attn_merge_partials",
-           "quantize_e4m3", "quantize_e4m3_hadamard", "attn_status_string", "flash_attn_func",
+           "quantize_e4m3", "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2",
+           "attn_status_string", "flash_attn_func",
            "LIB_PATH",
            "EXPORTED_SYMBOLS"]
 
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
                     "attn_merge_partials", "quantize_e4m3", "quantize_e4m3_hadamard",
-                    "attn_fwd_causal_offset_fp8_rounded_lse", "attn_status_string")
+                    "attn_fwd_causal_offset_fp8_rounded_lse", "quantize_e4m3_q_pow2",
+                    "attn_status_string")
 
 ATTN_OK = 0
 ATTN_E_INVAL = -1
@@ -68,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.attn_merge_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
     L.attn_merge_partials.restype = i
     L.quantize_e4m3.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    L.quantize_e4m3_q_pow2.argtypes = [vp, vp, vp, i, i, i, i, i, vp, i, f, vp]
+    L.quantize_e4m3_q_pow2.restype = i
     L.quantize_e4m3.restype = i
     L.quantize_e4m3_hadamard.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     L.quantize_e4m3_hadamard.restype = i
@@ -135,6 +139,18 @@ def quantize_e4m3(x, out, descale, per_head: bool, stream=None) -> None:
     st = load_library().quantize_e4m3(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
                                       int(bool(per_head)), _stream(stream))
     _check(st, "quantize_e4m3")
+
+
+def quantize_e4m3_q_pow2(x, out, descale, k_descale, softmax_scale: float, per_head: bool,
+                         stream=None) -> None:
+    """quantize_e4m3 of Q with the descale that makes the FP8 softmax constant (with K's
+    descales k_descale, (Hkv,) or (1,)) a power of two."""
+    B, N, H, d = (int(s) for s in x.shape)
+    Hkv = int(k_descale.numel()) if per_head else 1
+    st = load_library().quantize_e4m3_q_pow2(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
+                                             int(bool(per_head)), _ptr(k_descale), Hkv,
+                                             float(softmax_scale), _stream(stream))
+    _check(st, "quantize_e4m3_q_pow2")
 
 
 def quantize_e4m3_hadamard(x, out, descale, per_head: bool, stream=None) -> None:

@@ -170,6 +170,24 @@ int quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N, in
   return quantize_impl(x, out, descale, B, N, H, d, per_head, 0, stream);
 }
 
+int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale, int B, int N, int H,
+                         int d, int per_head, const float* k_descale, int Hkv,
+                         float softmax_scale, void* stream) {
+  if (!x || !out || !descale || !k_descale) return ATTN_E_INVAL;
+  if (B < 1 || N < 1 || H < 1 || d < 4 || (d & 3) != 0) return ATTN_E_INVAL;
+  if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
+  if (H > 65535 || Hkv < 1 || (per_head && H % Hkv != 0)) return ATTN_E_INVAL;
+  if (!(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_E_INVAL;
+  if ((long long)B * N * H * d >= kMaxElems) return ATTN_E_INVAL;
+  if (!aligned(x, 16) || !aligned(out, 4) || !aligned(descale, 4) || !aligned(k_descale, 4))
+    return ATTN_E_ALIGN;
+  const int st = check_device();
+  if (st != ATTN_OK) return st;
+  return launch_status(attn::launch_quantize_e4m3_q_pow2(x, out, descale, B, N, H, d, per_head,
+                                                         k_descale, Hkv, softmax_scale,
+                                                         (hipStream_t)stream));
+}
+
 int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, int N, int H,
                            int d, int per_head, void* stream) {
   return quantize_impl(x, out, descale, B, N, H, d, per_head, 1, stream);

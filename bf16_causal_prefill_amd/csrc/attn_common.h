@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int DV = 128;    // value head dim (both supported shapes)
 constexpr float LOG2E = 1.4426950408889634f;

@@ -126,6 +126,22 @@ void attn_fwd_kernel(FwdParams p) {
     vds = p.vds[p.per_head ? hkv : 0];
     c *= dq * dk;
   }
+  // FP8 with the exact LSE, c within 4 ulps of a power of two 2^ce (a relative change
+  // below 2^-21, the size of the rounding already in c's float32 product; a Q descale
+  // chosen for it makes this the case): the Q operand's E8M0 scale applies c inside the
+  // matrix instruction and its first k-step starts from -r_run, the running max in log2
+  // units, so the scores leave the MFMA as the exponent arguments themselves and the
+  // softmax phase needs no FMA per score.  Otherwise qsc is 1.0 and init16 stays zero.
+  bool P2 = false;
+  int qsc = 0x7f7f7f7f;   // E8M0 scale of the Q operand, one byte per 32-element block
+  if constexpr (EXACT) {
+    const uint32_t cb = __float_as_uint(c);
+    const uint32_t man = cb & 0x7fffffu;
+    const int ce = (int)((cb >> 23) & 0xffu) - 127 + (man >= 0x400000u ? 1 : 0);
+    P2 = ((cb >> 23) & 0xffu) != 0u && ((cb >> 23) & 0xffu) != 0xffu &&
+         (man <= 4u || man >= 0x7ffffcu) && ce >= -120 && ce <= 120;
+    if (P2) qsc = (127 + ce) * 0x01010101;
+  }
 
   // ---- Q^T fragments (B operand), held for the whole key loop -------------------
   // Rows past Nq read row Nq-1 (finite data); their outputs are never stored.
@@ -195,6 +211,7 @@ void attn_fwd_kernel(FwdParams p) {
   float l_run = 0.f;         // row sum relative to m_run (FP8: of the rounded P, full row;
                              // BF16: this lane's keys only)
   float lx_run = 0.f;        // FP8 + LSE: exact row sum over this lane's keys
+  float r_run = 0.f;         // FP8 + LSE with P2: running max in log2 units (c m)
 
   // Query row i sees keys 0 .. min(i + q_off, Nk - 1).
   const int wg_end = min(q0 + C::BM, Nq);
@@ -232,6 +249,7 @@ void attn_fwd_kernel(FwdParams p) {
   f32x16 zero16;
 #pragma unroll
   for (int i = 0; i < 16; ++i) zero16[i] = 0.f;
+  f32x16 init16 = zero16;       // first-k-step accumulator of Q K^T: -r_run with P2
 
   // Transposing V reads.  A P V MFMA needs, in lane l, channel 32md + l%32 of the keys
   // whose probabilities lane l holds, in the order it holds them:
@@ -341,8 +359,12 @@ void attn_fwd_kernel(FwdParams p) {
       const int jj = j - NPV, ks = jj / C::MT, m = jj % C::MT;
       if (ks == 0) {
         if constexpr (FP8) {
-          s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f, *(const i32x8*)&qf[ks], zero16, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+          if constexpr (EXACT)
+            s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f, *(const i32x8*)&qf[ks], init16, 0, 0, 0, 0x7f7f7f7f, 0, qsc);
+          else
+            s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f, *(const i32x8*)&qf[ks], zero16, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
         } else {
           s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, *(const bf16x8*)&qf[ks], zero16,
                                                          0, 0, 0);
@@ -350,7 +372,8 @@ void attn_fwd_kernel(FwdParams p) {
       } else {
         if constexpr (FP8) {
           s[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f, *(const i32x8*)&qf[ks], s[m], 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+              f, *(const i32x8*)&qf[ks], s[m], 0, 0, 0, 0x7f7f7f7f, 0,
+              EXACT ? qsc : 0x7f7f7f7f);
         } else {
           s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, *(const bf16x8*)&qf[ks], s[m],
                                                          0, 0, 0);
@@ -488,7 +511,71 @@ void attn_fwd_kernel(FwdParams p) {
       for (int e = 0; e < 8; ++e) pfb[kk][e] = (__bf16)0.f;
   };
 
-  auto valu_phase = [&](int t) {
+  // Softmax phase of the P2 path: the scores are x = c S - r_run already.  The first
+  // tile sets r_run to its row max; later a row moves it only when its tile max exceeds
+  // it by more than TAU.  The block exponent goes into the scaled conversion
+  // (v_cvt_scalef32_pk_fp8_f32 converts x / 2^-kb), so the exponentials and their fp32
+  // sums are taken on the unscaled arguments.
+  auto valu_p2 = [&](int t, float* bmx, float mx) {
+    if constexpr (!EXACT) return;
+    const bool first = t == 0;
+    if (first || __any(mx > TAU)) {
+      const float sh = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-sh);
+      r_run += sh;
+      lx_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < DV / 32; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+#pragma unroll
+      for (int m = 0; m < C::MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[m][i] -= sh;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) bmx[nb] -= sh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) init16[i] = -r_run;
+    }
+    float scl[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      // block maximum into (2^7, 2^8]; at most 126 so that the scale 2^-kb is a normal
+      // float (its exponent is the conversion's scale)
+      const int kb = (int)fminf(floorf(8.f - bmx[nb]), 126.f);
+      psc[nb] = 127 - kb;
+      scl[nb] = __uint_as_float((uint32_t)(127 - kb) << 23);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        s[2 * nb + (e >> 4)][e & 15] = __builtin_amdgcn_exp2f(s[2 * nb + (e >> 4)][e & 15]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      float bs[4];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * w + j;
+          pv[j] = s[2 * nb + (e >> 4)][e & 15];
+          bs[j] = w == 0 ? pv[j] : bs[j] + pv[j];
+        }
+        const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s){0, 0}, pv[0], pv[1],
+                                                                 scl[nb], false);
+        const v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, pv[2], pv[3], scl[nb], true);
+        pf8[nb][w] = __builtin_bit_cast(int, hi);
+      }
+      lx_run += (bs[0] + bs[1]) + (bs[2] + bs[3]);
+    }
+  };
+
+  auto valu_phase = [&](int t, auto p2_tag) {
+    constexpr bool PP = decltype(p2_tag)::value;
     __builtin_amdgcn_s_setprio(0);
     if (t >= w_kt) {        // past this wave's last tile: the next P V adds nothing
       zero_p();
@@ -529,6 +616,10 @@ void attn_fwd_kernel(FwdParams p) {
     float mx = bmx[0];
 #pragma unroll
     for (int nb = 1; nb < C::NB; ++nb) mx = fmaxf(mx, bmx[nb]);
+    if constexpr (EXACT && PP) {
+      valu_p2(t, bmx, mx);
+      return;
+    }
     // lazy running max: rescale only when some row's tile max exceeds m by > TAU
     if (__any((mx - m_run) * c > TAU)) {
       // (FP8 block maxima already cover both lane halves of the query)
@@ -650,16 +741,30 @@ void attn_fwd_kernel(FwdParams p) {
   phase_barrier();
   if (grp_b) phase_barrier();           // group B runs half a phase behind group A
 
-  for (int t = 0; t <= n_kt; ++t) {
-    mfma_phase(t);
-    wait_vmcnt<NDMA>();
-    phase_barrier();
-    if (t < n_kt) {
-      valu_phase(t);
-      wait_vmcnt<NDMA>();
-      phase_barrier();
-    }
+  // The P2 choice is taken once per workgroup, outside the key loop: each loop copy
+  // holds the registers of its own softmax path only (a loop wrapped in a lambda spills,
+  // hence the macro).
+#define ATTN_KEY_LOOP(P2_TAG)                \
+  for (int t = 0; t <= n_kt; ++t) {          \
+    mfma_phase(t);                           \
+    wait_vmcnt<NDMA>();                      \
+    phase_barrier();                         \
+    if (t < n_kt) {                          \
+      valu_phase(t, P2_TAG);                 \
+      wait_vmcnt<NDMA>();                    \
+      phase_barrier();                       \
+    }                                        \
   }
+  if constexpr (EXACT) {
+    if (P2) {
+      ATTN_KEY_LOOP(std::true_type{})
+    } else {
+      ATTN_KEY_LOOP(std::false_type{})
+    }
+  } else {
+    ATTN_KEY_LOOP(std::false_type{})
+  }
+#undef ATTN_KEY_LOOP
   wait_vmcnt<0>();                      // no copy into LDS outlives the loop
   if (!grp_b) phase_barrier();          // equal barrier counts in both groups
   __builtin_amdgcn_s_setprio(0);
@@ -684,7 +789,7 @@ void attn_fwd_kernel(FwdParams p) {
       }
     if (WANT_LSE && g == 0)
       p.lse[((size_t)b * p.Hq + h) * Nq + qrow] =
-          (m_run * c + __builtin_amdgcn_logf(lsum)) * LN2;
+          ((EXACT && P2 ? r_run : m_run * c) + __builtin_amdgcn_logf(lsum)) * LN2;
   }
 }
 

@@ -37,5 +37,9 @@ hipError_t launch_attn_merge(const void* o_a, const float* lse_a, const void* o_
 // Hadamard-rotated values (hadamard != 0).
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,
                                 int H, int d, int per_head, int hadamard, hipStream_t stream);
+hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale, int B,
+                                       int N, int H, int d, int per_head,
+                                       const float* k_descale, int Hkv, float softmax_scale,
+                                       hipStream_t stream);
 
 }  // namespace attn

@@ -269,17 +269,20 @@ __device__ __forceinline__ void encode_column(const float4* src, uint32_t* dst, 
   }
 }
 
+// amax_bits holds the absmax bits (ds_final == 0) or the finished descale (ds_final == 1).
 template <int HB4>
 __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
                                                        uint32_t* __restrict__ out,
                                                        const uint32_t* amax_bits, int rows,
-                                                       int L4, int d4, int per_head, int band) {
+                                                       int L4, int d4, int per_head, int band,
+                                                       int ds_final) {
   const int lane = threadIdx.x & 63;
   const int r0 = blockIdx.x * band;
   const int r1 = min(rows, r0 + band);
-  const float ds_t = per_head ? 0.f : descale_of(amax_bits[0]);
+  auto ds_of = [&](uint32_t bits) { return ds_final ? __uint_as_float(bits) : descale_of(bits); };
+  const float ds_t = per_head ? 0.f : ds_of(amax_bits[0]);
   for (int c = threadIdx.x; c < L4; c += QZ_THREADS) {
-    const float ds = per_head ? descale_of(amax_bits[c / d4]) : ds_t;
+    const float ds = per_head ? ds_of(amax_bits[c / d4]) : ds_t;
     const float4* src = (const float4*)x + (size_t)r0 * L4 + c;
     uint32_t* dst = out + (size_t)r0 * L4 + c;
     if (fast_divisor(ds))
@@ -287,6 +290,44 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     else
       encode_column<HB4, false>(src, dst, r0, r1, L4, ds, lane);
   }
+}
+
+// Q descale for which the FP8 attention's float32 softmax constant
+// c = fl(fl(scale * log2 e) * fl(dq * dk)) lies within 4 ulps of a power of two: the
+// smallest power of two at or above fl(fl(absmax / 448) * fl(sl * dk)), sl =
+// fl(scale * log2 e), divided by fl(sl * dk), then moved one ulp at a time (at most 16)
+// towards it until c is there.  A zero or non-finite absmax, or no such descale, gives
+// the plain absmax / 448 (1 for zero).  Every step is one float32 operation, correctly
+// rounded, so the result is reproducible off the device.
+__device__ __forceinline__ float pow2_q_descale(float amax, float dk, float sl) {
+  const float plain = amax > 0.f ? amax / 448.f : 1.f;
+  if (!(isfinite(amax) && amax > 0.f && isfinite(dk) && dk > 0.f)) return plain;
+  const float a = sl * dk;
+  const float tmin = (amax / 448.f) * a;
+  if (!(isfinite(tmin) && tmin > 0.f)) return plain;
+  const uint32_t b = __float_as_uint(tmin);
+  const uint32_t ex = (b >> 23) & 0xffu;
+  if (ex == 0u || ex >= 0xfeu) return plain;
+  const float target = (b & 0x7fffffu) == 0u ? tmin : __uint_as_float((ex + 1u) << 23);
+  float d = target / a;
+  for (int i = 0; i < 16; ++i) {
+    const float c = sl * (d * dk);
+    const uint32_t cb = __float_as_uint(c), cm = cb & 0x7fffffu, ce = (cb >> 23) & 0xffu;
+    if (ce != 0u && ce != 0xffu && (cm <= 4u || cm >= 0x7ffffcu) &&
+        fabsf(c / target - 1.f) < 0x1p-20f)
+      return d;
+    d = __uint_as_float(__float_as_uint(d) + (c < target ? 1u : 0xffffffffu));   // +-1 ulp
+  }
+  return plain;
+}
+
+// descale[i] <- the Q descale above from the absmax it holds (as float bits, which for a
+// non-negative float are the float itself); query head (or tensor) i pairs with
+// k_descale[i / group].
+__global__ void qz_finalize_q_pow2(float* descale, int n, const float* k_descale, int group,
+                                   float sl) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) descale[i] = pow2_q_descale(descale[i], k_descale[i / group], sl);
 }
 
 // descale = (absmax / 448) * post, post = 1 or the Hadamard normalisation 1/sqrt(hb).
@@ -301,7 +342,7 @@ static void qz_passes(const float* x, uint8_t* out, uint32_t* bits, int rows, in
   hipLaunchKernelGGL(qz_absmax<HB4>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4,
                      d4, H, per_head, band);
   hipLaunchKernelGGL(qz_encode<HB4>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
-                     (const uint32_t*)bits, rows, L4, d4, per_head, band);
+                     (const uint32_t*)bits, rows, L4, d4, per_head, band, 0);
 }
 
 hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, int B, int N,
@@ -330,6 +371,28 @@ hipError_t launch_quantize_e4m3(const float* x, uint8_t* out, float* descale, in
   }
   hipLaunchKernelGGL(qz_finalize, dim3((ns + 255) / 256), dim3(256), 0, stream, descale, ns,
                      post);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale, int B,
+                                       int N, int H, int d, int per_head,
+                                       const float* k_descale, int Hkv, float softmax_scale,
+                                       hipStream_t stream) {
+  const int rows = B * N;
+  const int ns = per_head ? H : 1;
+  const int group = per_head ? H / Hkv : 1;
+  const int L4 = H * (d / 4), d4 = d / 4;
+  const int band = (rows + QZ_TARGET_WGS - 1) / QZ_TARGET_WGS;
+  const int nwg = (rows + band - 1) / band;
+  uint32_t* bits = (uint32_t*)descale;
+  const float sl = softmax_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(qz_clear, dim3((ns + 255) / 256), dim3(256), 0, stream, bits, ns);
+  hipLaunchKernelGGL(qz_absmax<0>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, bits, rows, L4,
+                     d4, H, per_head, band);
+  hipLaunchKernelGGL(qz_finalize_q_pow2, dim3((ns + 255) / 256), dim3(256), 0, stream, descale,
+                     ns, k_descale, group, sl);
+  hipLaunchKernelGGL(qz_encode<0>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
+                     (const uint32_t*)bits, rows, L4, d4, per_head, band, 1);
   return hipGetLastError();
 }
 

@@ -11,7 +11,9 @@ Contents
 --------
 formats    -- exact decoders for bf16 and OCP e4m3fn codes, a round-to-nearest-
               even saturating e4m3 encoder, absmax quantisation, and the same
-              after a block Hadamard rotation (float32 butterflies).
+              after a block Hadamard rotation (float32 butterflies), and Q
+              quantisation with a descale that makes the FP8 softmax constant a
+              power of two.
 attention  -- the plain definition of causal softmax attention in float64
               (whole-row softmax, no online/tiled evaluation), over all rows or
               over sampled (b, h, i) rows; the same with Nq queries over Nk keys
@@ -25,12 +27,13 @@ inputs.  No function here is "parity unpinned".
 """
 from .formats import (bf16_decode, e4m3_decode, e4m3_encode, quantize_e4m3,
                       absmax_descale, encode_with_descale, E4M3_MAX, hadamard_block,
-                      hadamard_unnormalised_fp32, quantize_e4m3_hadamard)
+                      hadamard_unnormalised_fp32, quantize_e4m3_hadamard,
+                      quantize_e4m3_q_pow2, pow2_q_descale_one)
 from .attention import (causal_attention, causal_attention_rows, kv_head_of,
                         merge_partials, offset_attention, visible_keys)
 
 __all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "absmax_descale",
            "encode_with_descale", "E4M3_MAX", "hadamard_block", "hadamard_unnormalised_fp32",
-           "quantize_e4m3_hadamard",
+           "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2", "pow2_q_descale_one",
            "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys",
            "offset_attention", "merge_partials"]

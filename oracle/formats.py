@@ -101,6 +101,72 @@ def absmax_descale(x: np.ndarray, per_head: bool) -> np.ndarray:
     return np.where(amax > 0, descale, np.float32(1.0)).astype(np.float32)
 
 
+_LOG2E_F32 = np.float32(1.4426950408889634)
+
+
+def _near_pow2(c: np.float32) -> bool:
+    """c within 4 ulps of a power of two (mantissa field at most 4 above or below)."""
+    b = int(np.float32(c).view(np.uint32))
+    e, man = (b >> 23) & 0xFF, b & 0x7FFFFF
+    return 0 < e < 0xFF and (man <= 4 or man >= 0x7FFFFC)
+
+
+def pow2_q_descale_one(amax: np.float32, dk: np.float32, scale: float) -> np.float32:
+    """One Q descale for which the FP8 softmax constant, evaluated in float32 as
+    c = fl(fl(scale * log2 e) * fl(dq * dk)), lies within 4 ulps of a power of two:
+    the power of two is the smallest at or above fl(fl(amax / 448) * fl(fl(scale *
+    log2 e) * dk)), dq starts at fl(target / fl(fl(scale * log2 e) * dk)) and moves one
+    ulp at a time (at most 16) towards the target until c is there.  An all-zero (or
+    non-finite) absmax, or no such dq, gives the plain absmax descale."""
+    amax, dk = np.float32(amax), np.float32(dk)
+    plain = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    if not (np.isfinite(amax) and amax > 0 and np.isfinite(dk) and dk > 0):
+        return plain
+    sl = np.float32(np.float32(scale) * _LOG2E_F32)
+    a = np.float32(sl * dk)
+    tmin = np.float32(np.float32(amax / np.float32(E4M3_MAX)) * a)
+    if not (np.isfinite(tmin) and tmin > 0):
+        return plain
+    b = int(tmin.view(np.uint32))
+    exp = (b >> 23) & 0xFF
+    if exp == 0 or exp >= 0xFE:
+        return plain
+    target = tmin if (b & 0x7FFFFF) == 0 else np.uint32((exp + 1) << 23).view(np.float32)
+    target = np.float32(target)
+    d = np.float32(target / a)
+    for _ in range(16):
+        c = np.float32(sl * np.float32(d * dk))
+        if _near_pow2(c) and abs(float(c) / float(target) - 1.0) < 2.0 ** -20:
+            return d
+        d = np.nextafter(d, np.float32(np.inf) if c < target else np.float32(0))
+    return plain
+
+
+def quantize_e4m3_q_pow2(x: np.ndarray, per_head: bool, k_descale: np.ndarray,
+                         softmax_scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """Quantisation of Q whose descales make the FP8 softmax constant a power of two
+    (reading: any descale at or above absmax / 448 keeps every value in range; this one
+    lets the kernel apply the constant through the matrix instruction's power-of-two
+    operand scale).  k_descale: K's descales, one (per tensor) or Hkv (per head);
+    query head h pairs with KV head h / (H / Hkv).  Codes are the e4m3 rounding of
+    x / descale, as in quantize_e4m3."""
+    x = np.asarray(x, dtype=np.float32)
+    H = x.shape[2]
+    a = np.abs(x)
+    a = np.where(np.isnan(a), np.float32(0.0), a)
+    amax = (np.max(a, axis=(0, 1, 3)) if per_head else np.array([np.max(a)])).astype(np.float32)
+    kd = np.asarray(k_descale, dtype=np.float32).ravel()
+    if per_head:
+        g = H // len(kd)
+        descale = np.array([pow2_q_descale_one(amax[h], kd[h // g], softmax_scale)
+                            for h in range(H)], dtype=np.float32)
+        ds = descale[None, None, :, None]
+    else:
+        descale = np.array([pow2_q_descale_one(amax[0], kd[0], softmax_scale)], np.float32)
+        ds = descale[0]
+    return encode_with_descale(x, ds), descale
+
+
 def encode_with_descale(x: np.ndarray, descale) -> np.ndarray:
     """e4m3 codes of the float32 quotient x / descale (descale broadcast
     against x; float32 / float32 is correctly rounded)."""

@@ -163,3 +163,4 @@ def check(name: str, prec: str, o, ref_o, lse=None, ref_lse=None, lse_bound=None
 
 def inputs(w: workloads.Workload):
     return workloads.generate(w)
+

@@ -99,6 +99,23 @@ def test_quantize_rejects(name):
     assert q(o=A16 + 1) == ba.ATTN_E_ALIGN
 
 
+def test_quantize_q_pow2_rejects():
+    fn = ba.load_library().quantize_e4m3_q_pow2
+    vp = ctypes.c_void_p
+    q = lambda x=A16, o=A16, d_=A16, B=1, N=4, H=4, d=8, ph=1, kd=A16, Hkv=2, s=0.1: fn(
+        vp(x), vp(o), vp(d_), B, N, H, d, ph, vp(kd), Hkv, s, None)
+    assert q(kd=None) == ba.ATTN_E_INVAL
+    assert q(x=None) == ba.ATTN_E_INVAL
+    assert q(d=6) == ba.ATTN_E_INVAL
+    assert q(Hkv=0) == ba.ATTN_E_INVAL
+    assert q(Hkv=3) == ba.ATTN_E_INVAL            # H % Hkv != 0 with per-head scales
+    assert q(s=0.0) == ba.ATTN_E_INVAL
+    assert q(s=float("nan")) == ba.ATTN_E_INVAL
+    assert q(ph=2) == ba.ATTN_E_INVAL
+    assert q(kd=A16 + 2) == ba.ATTN_E_ALIGN
+    assert q(x=A16 + 4) == ba.ATTN_E_ALIGN
+
+
 def _no_device():
     import torch
     return torch.cuda.device_count() == 0

@@ -95,6 +95,31 @@ def test_quantize_degenerate(case):
         assert np.isinf(ds_h[2 if per_head else 0])
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("shape", [(1, 300, 8, 128, 2), (2, 77, 4, 192, 4), (1, 16, 6, 8, 3)])
+def test_quantize_q_pow2_bit_exact(shape, per_head):
+    """quantize_e4m3_q_pow2 against the oracle's rule: descales bit-identical (also for
+    an all-zero head), codes bit-identical; K's descales come from the oracle."""
+    B, N, H, d, Hkv = shape
+    note(f"case quantize_q_pow2 {shape} per_head={per_head}")
+    rng = np.random.default_rng(sum(shape) + per_head)
+    x = (rng.standard_normal((B, N, H, d)) * rng.uniform(1e-3, 40, H)[None, None, :, None]
+         ).astype(np.float32)
+    if per_head:
+        x[:, :, 1, :] = 0.0
+    k = rng.standard_normal((B, N, Hkv, d)).astype(np.float32) * np.float32(3.0)
+    _, kd = oracle.quantize_e4m3(k, per_head)
+    scale = 1.0 / np.sqrt(d)
+    ch, dh = oracle.quantize_e4m3_q_pow2(x, per_head, kd, scale)
+    xd = torch.from_numpy(x).to(DEV)
+    codes = torch.empty(x.shape, device=DEV, dtype=torch.uint8)
+    ds = torch.empty(H if per_head else 1, device=DEV, dtype=torch.float32)
+    ba.quantize_e4m3_q_pow2(xd, codes, ds, torch.from_numpy(kd).to(DEV), scale, per_head)
+    torch.cuda.synchronize()
+    assert np.array_equal(ds.cpu().numpy().view(np.uint32), dh.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), ch)
+
+
 # ---- extreme score patterns ------------------------------------------------------------
 
 def _slope_inputs(N: int, slope_log2: float, seed: int):

@@ -15,6 +15,8 @@ import workloads
 from gpu_harness import (bf16_bytes, check, fp8_score_error_bound, gpu_quantize, note,
                          run_bf16, run_fp8)
 
+import bf16_causal_prefill_amd as ba
+
 pytestmark = pytest.mark.gpu
 
 W = workloads.CONFIGS
@@ -276,3 +278,68 @@ def test_fp8_matrix_accumulation_model():
     note(f"fp8 accumulation pin: lse0={lse0} (exact 16399, grouped model 16392)")
     assert abs(lse0 - 16392.0) < 0.5
     assert np.all(out.o == 1.0)
+
+
+# ---- FP8 with a power-of-two softmax constant ------------------------------------------
+# When scale * log2(e) * dq * dk is (within 4 ulps) a power of two, the FP8 kernel with
+# the LSE applies it through the Q operand's matrix-instruction scale and starts the
+# first k-step from minus the running max, so the scores leave the matrix instruction as
+# exponent arguments.  quantize_e4m3_q_pow2 picks such a Q descale (at or above
+# absmax/448, by less than 2x).
+
+def _pow2_fp8_inputs(x, w):
+    """K and V quantised as usual, Q by quantize_e4m3_q_pow2 against K's descales, all on
+    the GPU and each asserted bit-identical to the oracle; returns device (codes,
+    descale) pairs and the oracle's decoded float64 tensors."""
+    host_c, host_d = {}, {}
+    for n in "kv":
+        host_c[n], host_d[n] = oracle.quantize_e4m3(x[n], w.fp8_per_head)
+    host_c["q"], host_d["q"] = oracle.quantize_e4m3_q_pow2(x["q"], w.fp8_per_head, host_d["k"],
+                                                           w.softmax_scale)
+    dev = {}
+    for n in "kv":
+        dev[n] = gpu_quantize(x[n], w.fp8_per_head)
+    qx = torch.from_numpy(x["q"]).to("cuda:0")
+    qc = torch.empty(x["q"].shape, device="cuda:0", dtype=torch.uint8)
+    qd = torch.empty((w.Hq if w.fp8_per_head else 1,), device="cuda:0", dtype=torch.float32)
+    ba.quantize_e4m3_q_pow2(qx, qc, qd, dev["k"][1], w.softmax_scale, w.fp8_per_head)
+    torch.cuda.synchronize()
+    dev["q"] = (qc, qd)
+    for n in "qkv":
+        assert np.array_equal(dev[n][0].cpu().numpy(), host_c[n]), n
+        assert np.array_equal(dev[n][1].cpu().numpy().view(np.uint32), host_d[n].view(np.uint32)), n
+    bc = (lambda d: d[None, None, :, None].astype(np.float64)) if w.fp8_per_head else \
+        (lambda d: float(d[0]))
+    host = [oracle.e4m3_decode(host_c[n]) * bc(host_d[n]) for n in "qkv"]
+    return [dev[n] for n in "qkv"], host
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_fp8_pow2_softmax_constant(case):
+    w = SMALL[case]
+    note(f"case fp8 pow2 {case}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d_qk}/{w.d_v}")
+    x = workloads.generate(w)
+    dev, (q, k, v) = _pow2_fp8_inputs(x, w)
+    (qc, qd), (kc, kd), (vc, vd) = dev
+    outs = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale, repeats=2)
+    assert outs[0].o_bytes == outs[1].o_bytes and outs[0].lse_bytes == outs[1].lse_bytes
+    ro, rl = oracle.causal_attention(q, k, v, w.softmax_scale)
+    check(f"{case}/pow2", "fp8", outs[0].o, ro, outs[0].lse, rl,
+          lse_bound=_outlier_bound(w, q, k, rl.shape))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fp8_pow2_full_size_sampled_rows(name):
+    w = W[name]
+    note(f"case fp8 pow2 full {name}: N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk}/{w.d_v}")
+    x = workloads.generate(w)
+    rows = _sample_rows(w)
+    dev, (q, k, v) = _pow2_fp8_inputs(x, w)
+    (qc, qd), (kc, kd), (vc, vd) = dev
+    out = run_fp8(qc, kc, vc, qd, kd, vd, w.fp8_per_head, w.softmax_scale)[0]
+    ro, rl = oracle.causal_attention_rows(q, k, v, w.softmax_scale, rows)
+    bb, hh, ii = (np.array([r[j] for r in rows]) for j in range(3))
+    go, gl = out.o[bb, ii, hh], out.lse[bb, hh, ii]
+    assert np.all(np.isfinite(out.o)) and np.all(np.isfinite(out.lse))
+    check(f"{name}/pow2/rows", "fp8", go, ro, gl, rl,
+          lse_bound=_outlier_bound(w, q, k, gl.shape, rows))

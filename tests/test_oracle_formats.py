@@ -154,6 +154,40 @@ def test_quantize_nan_and_inf_elements(per_head):
     assert np.array_equal(cz[sl][finite] >> 7, np.signbit(z[sl][finite]).astype(np.uint8))
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_q_pow2(per_head):
+    """The Q descale that makes the FP8 softmax constant a power of two: the float32
+    constant fl(fl(s log2 e) fl(dq dk)) lies within 4 ulps of the smallest power of two
+    at or above s log2(e) absmax/448 dk, so dq is at or above absmax/448 (by less than
+    2x, to a few ulps), codes decode to x within half an e4m3 step of that descale, and
+    an all-zero head keeps descale 1."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv = 6, 3
+    for scale in (1 / np.sqrt(128), 1 / np.sqrt(192), 0.25):
+        x = (rng.standard_normal((1, 40, Hq, 16)) * rng.uniform(1e-3, 30, Hq)[None, None, :, None]
+             ).astype(np.float32)
+        if per_head:
+            x[:, :, 4, :] = 0.0
+        kd = rng.uniform(1e-4, 1.0, Hkv if per_head else 1).astype(np.float32)
+        codes, dq = oracle.quantize_e4m3_q_pow2(x, per_head, kd, scale)
+        _, plain = oracle.quantize_e4m3(x, per_head)
+        sl = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+        for h in range(len(dq)):
+            if plain[h] == 1.0 and per_head and h == 4:
+                assert dq[h] == 1.0
+                continue
+            k = kd[h // (Hq // Hkv)] if per_head else kd[0]
+            c = np.float32(sl * np.float32(dq[h] * k))
+            m, e = np.frexp(np.float64(c))
+            target = 2.0 ** int(np.ceil(np.log2(float(sl) * float(plain[h]) * float(k))))
+            assert abs(float(c) / target - 1) <= 4 * 2.0 ** -23, (c, target)
+            assert plain[h] * (1 - 2.0 ** -20) <= dq[h] < 2 * plain[h] * (1 + 2.0 ** -20)
+        ds = dq[None, None, :, None] if per_head else dq[0]
+        back = oracle.e4m3_decode(codes) * ds
+        tol = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * ds) * 1.0001
+        assert np.all(np.abs(back - x) <= tol)
+
+
 # ---- Hadamard rotation before quantisation ----------------------------------------
 
 def _sylvester(n):

@@ -565,10 +565,12 @@ void attn_fwd_kernel(FwdParams p) {
           pv[j] = s[2 * nb + (e >> 4)][e & 15];
           bs[j] = w == 0 ? pv[j] : bs[j] + pv[j];
         }
-        const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s){0, 0}, pv[0], pv[1],
-                                                                 scl[nb], false);
-        const v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, pv[2], pv[3], scl[nb], true);
-        pf8[nb][w] = __builtin_bit_cast(int, hi);
+        // both halves are overwritten, so the first conversion writes into the register
+        // of a probability the sums have already read (no zeroed register is needed)
+        const v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            __builtin_bit_cast(v2s, pv[3]), pv[2], pv[3], scl[nb], true);
+        const v2s wd = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, pv[0], pv[1], scl[nb], false);
+        pf8[nb][w] = __builtin_bit_cast(int, wd);
       }
       lx_run += (bs[0] + bs[1]) + (bs[2] + bs[3]);
     }

@@ -90,6 +90,41 @@ def test_offset_fp8(case, want_lse):
     check(case, "fp8", go, ro, gl, rl if want_lse else None)
 
 
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_offset_fp8_pow2_q_scale(case):
+    """The offset entry point with the LSE on Q quantised by quantize_e4m3_q_pow2 (the
+    power-of-two softmax constant path, whose first tile sets the running max)."""
+    B, Nq, Nk, off, Hq, Hkv, dqk, per_head = CASES[case]
+    note(f"offset fp8 pow2 {case}: B={B} Nq={Nq} Nk={Nk} q_offset={off}")
+    q, k, v = _draw(case, B, Nq, Nk, Hq, Hkv, dqk)
+    scale = 1.0 / np.sqrt(dqk)
+    dev, dec, host_ds = {}, {}, {}
+    bc = (lambda d: d[None, None, :, None].astype(np.float64)) if per_head else \
+        (lambda d: float(d[0]))
+    for n, x in (("k", k), ("v", v)):
+        cd, dd = gpu_quantize(x, per_head)
+        ch, dh = oracle.quantize_e4m3(x, per_head)
+        assert np.array_equal(cd.cpu().numpy(), ch)
+        assert np.array_equal(dd.cpu().numpy().view(np.uint32), dh.view(np.uint32))
+        dev[n], dec[n], host_ds[n] = (cd, dd), oracle.e4m3_decode(ch) * bc(dh), dh
+    ch, dh = oracle.quantize_e4m3_q_pow2(q, per_head, host_ds["k"], scale)
+    qc = torch.empty(q.shape, device=DEV, dtype=torch.uint8)
+    qd = torch.empty((Hq if per_head else 1,), device=DEV, dtype=torch.float32)
+    ba.quantize_e4m3_q_pow2(torch.from_numpy(q).to(DEV), qc, qd, dev["k"][1], scale, per_head)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc.cpu().numpy(), ch)
+    assert np.array_equal(qd.cpu().numpy().view(np.uint32), dh.view(np.uint32))
+    dec["q"] = oracle.e4m3_decode(ch) * bc(dh)
+    o, lse = _empty_out(B, Nq, Hq)
+    ba.attn_fwd_causal_offset_fp8(qc, dev["k"][0], dev["v"][0], qd, dev["k"][1], dev["v"][1],
+                                  o, lse, q_offset=off, softmax_scale=scale,
+                                  descale_per_head=int(per_head))
+    torch.cuda.synchronize()
+    go, gl = _host(o, lse)
+    ro, rl = oracle.offset_attention(dec["q"], dec["k"], dec["v"], scale, off)
+    check(f"{case}/pow2", "fp8", go, ro, gl, rl)
+
+
 @pytest.mark.parametrize("prec", ["bf16", "fp8"])
 def test_offset_zero_square_is_plain_causal(prec):
     """Nq == Nk with q_offset 0 runs the same kernel as the plain entry point: the

@@ -101,17 +101,99 @@ def _check(status: int, where: str) -> None:
         raise AttnError(status, where)
 
 
-def _dims(q, k, v):
-    B, N, Hq, dqk = q.shape
-    Hkv = k.shape[2]
-    dv = v.shape[3]
-    return int(B), int(Hq), int(Hkv), int(N), int(dqk), int(dv)
+# ---- argument checks -----------------------------------------------------------------
+# Every wrapper checks dtypes, shapes, devices and contiguity before the library is
+# called, so a tensor that does not match what the kernels will index (a K/V with fewer
+# rows than Q, a descale with fewer values than heads, an output of the wrong size) is
+# reported as ValueError instead of being read or written past its end on the device.
+# Shapes and dtypes are checked first, then the device and the memory layout.
+
+def _dtypes(kind):
+    import torch
+    if kind == "bf16":
+        return (torch.bfloat16,)
+    if kind == "e4m3":
+        return (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    return (torch.float32,)
+
+
+def _want(t, name, kind, shape):
+    """t must be a tensor of one of `kind`'s dtypes with exactly `shape`."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "shape"):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype not in _dtypes(kind):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {kind}")
+    if tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _on_gpu(device, **tensors):
+    """Every given tensor is a contiguous tensor on `device` (a CUDA/HIP device)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{name} must be a GPU tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _rank4(t, name):
+    if t is None or not hasattr(t, "shape") or len(t.shape) != 4:
+        raise ValueError(f"{name} must be a 4-d (B, N, H, d) tensor")
+    return tuple(int(x) for x in t.shape)
+
+
+def _attn_shapes(q, k, v, kind, same_n):
+    """(B, Hq, Hkv, Nq, Nk, dqk, dv) of q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk), v (B,Nk,Hkv,dv)."""
+    B, Nq, Hq, dqk = _rank4(q, "q")
+    _, Nk, Hkv, _ = _rank4(k, "k")
+    dv = _rank4(v, "v")[3]
+    _want(q, "q", kind, (B, Nq, Hq, dqk))
+    _want(k, "k", kind, (B, Nk, Hkv, dqk))
+    _want(v, "v", kind, (B, Nk, Hkv, dv))
+    if same_n and Nk != Nq:
+        raise ValueError(f"k/v have {Nk} rows, q has {Nq}")
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    return B, Hq, Hkv, Nq, Nk, dqk, dv
+
+
+def _outputs(o, lse, B, Nq, Hq, dv, lse_required=False):
+    _want(o, "o", "bf16", (B, Nq, Hq, dv))
+    if lse is not None or lse_required:
+        _want(lse, "lse", "f32", (B, Hq, Nq))
+
+
+def _descales(q_descale, k_descale, v_descale, Hq, Hkv, per_head):
+    """Per-head choice (inferred from the sizes when per_head is None) and the check that
+    all three descales hold 1 value (per tensor) or Hq / Hkv / Hkv values (per head)."""
+    for n, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if t is None or not hasattr(t, "numel"):
+            raise ValueError(f"{n} is required")
+        if t.dtype not in _dtypes("f32"):
+            raise ValueError(f"{n}: dtype {t.dtype}, expected float32")
+    if per_head is None:
+        per_head = int(q_descale.numel() > 1 or k_descale.numel() > 1 or v_descale.numel() > 1)
+    per_head = int(bool(per_head))
+    want = (Hq, Hkv, Hkv) if per_head else (1, 1, 1)
+    got = (q_descale.numel(), k_descale.numel(), v_descale.numel())
+    if got != want:
+        raise ValueError(f"descales hold {got} values, expected {want} "
+                         f"(per {'head' if per_head else 'tensor'})")
+    return per_head
 
 
 def attn_fwd_causal_bf16(q, k, v, o, lse=None, softmax_scale=None, stream=None) -> None:
     """q (B,N,Hq,dqk), k (B,N,Hkv,dqk), v (B,N,Hkv,dv) bf16 -> o (B,N,Hq,dv) bf16,
     lse (B,Hq,N) float32 or None.  Tensors must be contiguous on the GPU."""
-    B, Hq, Hkv, N, dqk, dv = _dims(q, k, v)
+    B, Hq, Hkv, N, _, dqk, dv = _attn_shapes(q, k, v, "bf16", same_n=True)
+    _outputs(o, lse, B, N, Hq, dv)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_fwd_causal_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                              B, Hq, Hkv, N, dqk, dv, scale, _stream(stream))
@@ -122,10 +204,12 @@ def attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
                         softmax_scale=None, descale_per_head=None, stream=None) -> None:
     """q/k/v uint8 e4m3fn codes; *_descale float32 device tensors of 1 element
     (per tensor) or Hq / Hkv elements (per head)."""
-    B, Hq, Hkv, N, dqk, dv = _dims(q, k, v)
+    B, Hq, Hkv, N, _, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=True)
+    _outputs(o, lse, B, N, Hq, dv)
+    descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
+            v_descale=v_descale)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
-    if descale_per_head is None:
-        descale_per_head = int(q_descale.numel() > 1)
     st = load_library().attn_fwd_causal_fp8(
         _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, N, dqk, dv, scale,
@@ -133,9 +217,29 @@ def attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
     _check(st, "attn_fwd_causal_fp8")
 
 
+def _quant_args(x, out, descale, per_head, k_descale=None):
+    """Checks of the quantisers' arguments (k_descale: quantize_e4m3_q_pow2's);
+    returns (B, N, H, d, Hkv)."""
+    B, N, H, d = _rank4(x, "x")
+    _want(x, "x", "f32", (B, N, H, d))
+    _want(out, "out", "e4m3", (B, N, H, d))
+    _want(descale, "descale", "f32", (H if per_head else 1,))
+    Hkv = 1
+    if k_descale is not None:
+        if not hasattr(k_descale, "numel") or k_descale.dtype not in _dtypes("f32"):
+            raise ValueError("k_descale must be a float32 tensor")
+        Hkv = int(k_descale.numel()) if per_head else 1
+        if not per_head and k_descale.numel() != 1:
+            raise ValueError("k_descale must hold 1 value with per-tensor scales")
+        if Hkv < 1 or H % Hkv:
+            raise ValueError(f"H={H} is not a multiple of the {Hkv} KV-head descales")
+    _on_gpu(x.device, x=x, out=out, descale=descale, k_descale=k_descale)
+    return B, N, H, d, Hkv
+
+
 def quantize_e4m3(x, out, descale, per_head: bool, stream=None) -> None:
     """x float32 (B,N,H,d) -> out uint8 codes, descale float32 (H,) or (1,)."""
-    B, N, H, d = (int(s) for s in x.shape)
+    B, N, H, d, _ = _quant_args(x, out, descale, per_head)
     st = load_library().quantize_e4m3(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
                                       int(bool(per_head)), _stream(stream))
     _check(st, "quantize_e4m3")
@@ -145,8 +249,9 @@ def quantize_e4m3_q_pow2(x, out, descale, k_descale, softmax_scale: float, per_h
                          stream=None) -> None:
     """quantize_e4m3 of Q with the descale that makes the FP8 softmax constant (with K's
     descales k_descale, (Hkv,) or (1,)) a power of two."""
-    B, N, H, d = (int(s) for s in x.shape)
-    Hkv = int(k_descale.numel()) if per_head else 1
+    if k_descale is None:
+        raise ValueError("k_descale is required")
+    B, N, H, d, Hkv = _quant_args(x, out, descale, per_head, k_descale)
     st = load_library().quantize_e4m3_q_pow2(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
                                              int(bool(per_head)), _ptr(k_descale), Hkv,
                                              float(softmax_scale), _stream(stream))
@@ -156,17 +261,10 @@ def quantize_e4m3_q_pow2(x, out, descale, k_descale, softmax_scale: float, per_h
 def quantize_e4m3_hadamard(x, out, descale, per_head: bool, stream=None) -> None:
     """quantize_e4m3 of x rotated by H/sqrt(hb) per block of hb channels (for Q and K);
     code * descale is the rotated value."""
-    B, N, H, d = (int(s) for s in x.shape)
+    B, N, H, d, _ = _quant_args(x, out, descale, per_head)
     st = load_library().quantize_e4m3_hadamard(_ptr(x), _ptr(out), _ptr(descale), B, N, H, d,
                                                int(bool(per_head)), _stream(stream))
     _check(st, "quantize_e4m3_hadamard")
-
-
-def _dims_qk(q, k, v):
-    B, Nq, Hq, dqk = q.shape
-    Nk, Hkv = k.shape[1], k.shape[2]
-    dv = v.shape[3]
-    return int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(dqk), int(dv)
 
 
 def attn_fwd_causal_offset_bf16(q, k, v, o, lse=None, q_offset=None, softmax_scale=None,
@@ -174,7 +272,9 @@ def attn_fwd_causal_offset_bf16(q, k, v, o, lse=None, q_offset=None, softmax_sca
     """q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk), v (B,Nk,Hkv,dv) bf16 -> o (B,Nq,Hq,dv) bf16,
     lse (B,Hq,Nq) float32 or None.  Key j is visible to query i iff j <= i + q_offset
     (default Nk - Nq: the queries are the last Nq of the Nk positions)."""
-    B, Hq, Hkv, Nq, Nk, dqk, dv = _dims_qk(q, k, v)
+    B, Hq, Hkv, Nq, Nk, dqk, dv = _attn_shapes(q, k, v, "bf16", same_n=False)
+    _outputs(o, lse, B, Nq, Hq, dv)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse)
     off = Nk - Nq if q_offset is None else int(q_offset)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_fwd_causal_offset_bf16(
@@ -188,11 +288,13 @@ def attn_fwd_causal_offset_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse=
                                stream=None) -> None:
     """FP8 codes version of attn_fwd_causal_offset_bf16 (descales as for
     attn_fwd_causal_fp8)."""
-    B, Hq, Hkv, Nq, Nk, dqk, dv = _dims_qk(q, k, v)
+    B, Hq, Hkv, Nq, Nk, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=False)
+    _outputs(o, lse, B, Nq, Hq, dv, lse_required=False)
+    descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
+            v_descale=v_descale)
     off = Nk - Nq if q_offset is None else int(q_offset)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
-    if descale_per_head is None:
-        descale_per_head = int(q_descale.numel() > 1)
     st = load_library().attn_fwd_causal_offset_fp8(
         _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, off, dqk, dv, scale,
@@ -205,11 +307,13 @@ def attn_fwd_causal_offset_fp8_rounded_lse(q, k, v, q_descale, k_descale, v_desc
                                            descale_per_head=None, stream=None) -> None:
     """attn_fwd_causal_offset_fp8 on the rounded-probability path, also writing the LSE
     of the rounded row sum that normalises O (consistent with O, not the exact LSE)."""
-    B, Hq, Hkv, Nq, Nk, dqk, dv = _dims_qk(q, k, v)
+    B, Hq, Hkv, Nq, Nk, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=False)
+    _outputs(o, lse, B, Nq, Hq, dv, lse_required=True)
+    descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
+            v_descale=v_descale)
     off = Nk - Nq if q_offset is None else int(q_offset)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
-    if descale_per_head is None:
-        descale_per_head = int(q_descale.numel() > 1)
     st = load_library().attn_fwd_causal_offset_fp8_rounded_lse(
         _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, off, dqk, dv, scale,
@@ -220,7 +324,12 @@ def attn_fwd_causal_offset_fp8_rounded_lse(q, k, v, q_descale, k_descale, v_desc
 def attn_merge_partials(o_a, lse_a, o_b, lse_b, o, lse=None, stream=None) -> None:
     """Merge two partial attentions (bf16 o (B,N,Hq,dv), float32 lse (B,Hq,N)) of the
     same queries over disjoint key sets into o / lse (which may alias the inputs)."""
-    B, N, Hq, dv = (int(x) for x in o_a.shape)
+    B, N, Hq, dv = _rank4(o_a, "o_a")
+    for n, t in (("o_a", o_a), ("o_b", o_b), ("o", o)):
+        _want(t, n, "bf16", (B, N, Hq, dv))
+    for n, t in (("lse_a", lse_a), ("lse_b", lse_b)) + ((("lse", lse),) if lse is not None else ()):
+        _want(t, n, "f32", (B, Hq, N))
+    _on_gpu(o_a.device, o_a=o_a, lse_a=lse_a, o_b=o_b, lse_b=lse_b, o=o, lse=lse)
     st = load_library().attn_merge_partials(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
                                             _ptr(o), _ptr(lse), B, N, Hq, dv, _stream(stream))
     _check(st, "attn_merge_partials")

@@ -149,3 +149,113 @@ def test_rounded_lse_entry_requires_lse_and_validates():
     assert call(q=None) == ba.ATTN_E_INVAL
     assert call(dqk=64) == ba.ATTN_E_UNSUPPORTED
     assert call(q=A16 + 4) == ba.ATTN_E_ALIGN
+
+
+# ---- the Python binding's argument checks (CPU tensors; the library is never called) ----
+
+@pytest.fixture
+def no_library(monkeypatch):
+    """Any call into the library fails the test: the checks must come first."""
+    def boom(*a, **k):
+        raise AssertionError("the library was called before the arguments were checked")
+    monkeypatch.setattr(ba, "load_library", boom)
+
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _fp8_args(B=1, Nq=8, Nk=8, Hq=4, Hkv=2, d=128, dv=128, nq=4, nk=2, nv=2, lse=True):
+    import torch
+    return dict(q=_t((B, Nq, Hq, d), torch.uint8), k=_t((B, Nk, Hkv, d), torch.uint8),
+                v=_t((B, Nk, Hkv, dv), torch.uint8), q_descale=_t((nq,), torch.float32),
+                k_descale=_t((nk,), torch.float32), v_descale=_t((nv,), torch.float32),
+                o=_t((B, Nq, Hq, dv), torch.bfloat16),
+                lse=_t((B, Hq, Nq), torch.float32) if lse else None)
+
+
+FP8_BAD = {
+    "k_fewer_rows": (dict(Nk=4), "rows"),
+    "k_descale_one_value_per_head_q": (dict(nk=1), "descales"),
+    "v_descale_short": (dict(nv=1), "descales"),
+    "q_descale_short": (dict(nq=2), "descales"),
+    "heads_not_multiple": (dict(Hq=3, Hkv=2, nq=3), "multiple"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FP8_BAD))
+def test_binding_rejects_fp8_mismatch(no_library, case):
+    kw, msg = FP8_BAD[case]
+    with pytest.raises(ValueError, match=msg):
+        ba.attn_fwd_causal_fp8(**_fp8_args(**kw))
+
+
+def test_binding_rejects_fp8_wrong_outputs(no_library):
+    import torch
+    a = _fp8_args()
+    with pytest.raises(ValueError, match="o: shape"):
+        ba.attn_fwd_causal_fp8(**dict(a, o=_t((1, 8, 4, 64), torch.bfloat16)))
+    with pytest.raises(ValueError, match="o: dtype"):
+        ba.attn_fwd_causal_fp8(**dict(a, o=_t((1, 8, 4, 128), torch.float32)))
+    with pytest.raises(ValueError, match="lse: shape"):
+        ba.attn_fwd_causal_fp8(**dict(a, lse=_t((1, 8, 4), torch.float32)))
+    with pytest.raises(ValueError, match="q: dtype"):
+        ba.attn_fwd_causal_fp8(**dict(a, q=_t((1, 8, 4, 128), torch.bfloat16)))
+    with pytest.raises(ValueError, match="q_descale: dtype"):
+        ba.attn_fwd_causal_fp8(**dict(a, q_descale=_t((4,), torch.float64)))
+
+
+def test_binding_rejects_cpu_and_noncontiguous(no_library):
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.attn_fwd_causal_fp8(**_fp8_args())
+    q = _t((1, 8, 4, 128), torch.bfloat16)
+    k = _t((1, 8, 2, 128), torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.attn_fwd_causal_bf16(q, k, k.clone(), _t((1, 8, 4, 128), torch.bfloat16))
+    with pytest.raises(ValueError, match="rows"):
+        ba.attn_fwd_causal_bf16(q, k[:, :4], k[:, :4].clone(), _t((1, 8, 4, 128), torch.bfloat16))
+
+
+def test_binding_rejects_offset_and_rounded(no_library):
+    a = _fp8_args(Nq=4, Nk=8)
+    with pytest.raises(ValueError, match="lse is required"):
+        ba.attn_fwd_causal_offset_fp8_rounded_lse(**dict(a, lse=None))
+    with pytest.raises(ValueError, match="v: shape"):
+        b = _fp8_args(Nq=4, Nk=8)
+        b["v"] = b["v"][:, :5].clone()
+        ba.attn_fwd_causal_offset_fp8(**b)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.attn_fwd_causal_offset_fp8(**a)
+
+
+def test_binding_rejects_quantize_mismatch(no_library):
+    import torch
+    x = _t((1, 4, 3, 8), torch.float32)
+    out = _t((1, 4, 3, 8), torch.uint8)
+    with pytest.raises(ValueError, match="descale: shape"):
+        ba.quantize_e4m3(x, out, _t((1,), torch.float32), per_head=True)
+    with pytest.raises(ValueError, match="descale: shape"):
+        ba.quantize_e4m3_hadamard(x, out, _t((3,), torch.float32), per_head=False)
+    with pytest.raises(ValueError, match="out: shape"):
+        ba.quantize_e4m3(x, _t((1, 4, 3, 4), torch.uint8), _t((3,), torch.float32), True)
+    with pytest.raises(ValueError, match="x: dtype"):
+        ba.quantize_e4m3(x.double(), out, _t((3,), torch.float32), True)
+    with pytest.raises(ValueError, match="multiple"):
+        ba.quantize_e4m3_q_pow2(x, out, _t((3,), torch.float32), _t((2,), torch.float32),
+                                0.1, per_head=True)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.quantize_e4m3(x, out, _t((3,), torch.float32), True)
+
+
+def test_binding_rejects_merge_mismatch(no_library):
+    import torch
+    o = _t((1, 8, 4, 128), torch.bfloat16)
+    l = _t((1, 4, 8), torch.float32)
+    with pytest.raises(ValueError, match="o_b: shape"):
+        ba.attn_merge_partials(o, l, _t((1, 7, 4, 128), torch.bfloat16), l, o.clone())
+    with pytest.raises(ValueError, match="lse_b: shape"):
+        ba.attn_merge_partials(o, l, o.clone(), _t((1, 4, 7), torch.float32), o.clone())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.attn_merge_partials(o, l, o.clone(), l.clone(), o.clone())

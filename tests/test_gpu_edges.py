@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_harness import DEV, bf16_bytes, check, gpu_quantize, note, run_bf16, run_fp8
+from gpu_harness import DEV, abs_v, bf16_bytes, check, gpu_quantize, note, run_bf16, run_fp8
 
 import bf16_causal_prefill_amd as ba
 
@@ -168,10 +168,11 @@ def test_extreme_score_slopes(pattern, prec):
         (qc, qd), (kc, kd), (vc, vd) = dev
         out = run_fp8(qc, kc, vc, qd, kd, vd, False, scale, want_lse=prec == "fp8")[0]
     ro, rl = oracle.causal_attention(q, k, v, scale)
+    ra = abs_v(oracle.causal_attention, q, k, v, scale) if prec != "bf16" else None
     if prec == "fp8_nolse":
-        check(f"slope_{pattern}", "fp8", out.o, ro)
+        check(f"slope_{pattern}", "fp8", out.o, ro, ref_abs_o=ra, fp8_path="lean")
     else:
-        check(f"slope_{pattern}", prec, out.o, ro, out.lse, rl)
+        check(f"slope_{pattern}", prec, out.o, ro, out.lse, rl, ref_abs_o=ra, fp8_path="exact")
 
 
 # ---- the largest accepted launch ---------------------------------------------------------
@@ -193,16 +194,18 @@ def _oracle_rows_from_device(tensors, decoders, scale, rows):
     the whole multi-GiB tensors); decoders map a device slice to float64 values."""
     q, k, v = tensors
     ro = np.empty((len(rows), v.shape[3]))
+    ra = np.empty((len(rows), v.shape[3]))
     rl = np.empty(len(rows))
     by_b = {}
     for r, (b, h, i) in enumerate(rows):
         by_b.setdefault(b, []).append(r)
     for b, idx in by_b.items():
         qb, kb, vb = (dec(t[b:b + 1]) for dec, t in zip(decoders, tensors))
-        o1, l1 = oracle.causal_attention_rows(qb, kb, vb, scale,
-                                              [(0, rows[r][1], rows[r][2]) for r in idx])
+        sub = [(0, rows[r][1], rows[r][2]) for r in idx]
+        o1, l1 = oracle.causal_attention_rows(qb, kb, vb, scale, sub)
         ro[idx], rl[idx] = o1, l1
-    return ro, rl
+        ra[idx] = abs_v(oracle.causal_attention_rows, qb, kb, vb, scale, sub)
+    return ro, rl, ra
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp8"])
@@ -240,7 +243,7 @@ def test_largest_launch_sampled_rows(prec):
                          for s in descales)
     torch.cuda.synchronize()
     rows = _max_rows(np.random.default_rng(49))
-    ro, rl = _oracle_rows_from_device(tensors, decoders, scale, rows)
+    ro, rl, ra = _oracle_rows_from_device(tensors, decoders, scale, rows)
     bb = torch.tensor([r[0] for r in rows], device=DEV)
     hh = torch.tensor([r[1] for r in rows], device=DEV)
     ii = torch.tensor([r[2] for r in rows], device=DEV)
@@ -248,4 +251,5 @@ def test_largest_launch_sampled_rows(prec):
     gl = lse[bb, hh, ii].cpu().numpy().astype(np.float64)
     # every output element was written (the buffers started as NaN)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
-    check("largest_launch/rows", prec, go, ro, gl, rl)
+    check("largest_launch/rows", prec, go, ro, gl, rl, ref_abs_o=ra, fp8_path="exact",
+          row_heads=[(b, h) for b, h, _ in rows])

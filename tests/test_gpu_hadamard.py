@@ -12,7 +12,7 @@ import torch
 
 import bf16_causal_prefill_amd as ba
 import oracle
-from gpu_harness import DEV, FP8_REL_FRO, check, gpu_quantize, note, rel_fro, run_fp8
+from gpu_harness import DEV, FP8_REL_FRO, abs_v, check, gpu_quantize, note, rel_fro, run_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,8 @@ def test_fp8_attention_on_rotated_qk(d):
            for c, s in ((cq, dq), (ck, dk), (cv, dv))]
     g = run_fp8(rq[0], rk[0], pv[0], rq[1], rk[1], pv[1], per_head, scale)[0]
     ro, rl = oracle.causal_attention(*dec, scale)
-    check(f"rotated d={d}", "fp8", g.o, ro, g.lse, rl)
+    check(f"rotated d={d}", "fp8", g.o, ro, g.lse, rl, fp8_path="exact",
+          ref_abs_o=abs_v(oracle.causal_attention, *dec, scale))
     # Against the unrotated float32 inputs: the rotation is orthogonal, so what is left
     # is the quantisation error of Q, K and V.
     fo, _ = oracle.causal_attention(q, k, v, scale)

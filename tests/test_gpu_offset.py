@@ -13,7 +13,8 @@ import torch
 
 import bf16_causal_prefill_amd as ba
 import oracle
-from gpu_harness import (DEV, bf16_bytes, check, gpu_quantize, note, to_dev_u16_as_bf16)
+from gpu_harness import (DEV, ROUNDED_LSE_BOUND, abs_v, bf16_bytes, check, gpu_quantize, note,
+                         to_dev_u16_as_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +88,8 @@ def test_offset_fp8(case, want_lse):
     torch.cuda.synchronize()
     go, gl = _host(o, lse)
     ro, rl = oracle.offset_attention(*dec, scale, off)
-    check(case, "fp8", go, ro, gl, rl if want_lse else None)
+    check(case, "fp8", go, ro, gl, rl if want_lse else None, fp8_path="exact" if want_lse else "lean",
+          ref_abs_o=abs_v(oracle.offset_attention, *dec, scale, off))
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
@@ -122,7 +124,8 @@ def test_offset_fp8_pow2_q_scale(case):
     torch.cuda.synchronize()
     go, gl = _host(o, lse)
     ro, rl = oracle.offset_attention(dec["q"], dec["k"], dec["v"], scale, off)
-    check(f"{case}/pow2", "fp8", go, ro, gl, rl)
+    check(f"{case}/pow2", "fp8", go, ro, gl, rl, fp8_path="exact",
+          ref_abs_o=abs_v(oracle.offset_attention, dec["q"], dec["k"], dec["v"], scale, off))
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp8"])
@@ -218,7 +221,9 @@ def test_split_keys_and_merge_equals_causal(prec):
     torch.cuda.synchronize()
     go, gl = _host(oa, la)
     ro, rl = oracle.causal_attention(*dec, scale)
-    check(f"split-merge-{prec}", prec, go, ro[:, P:], gl, rl[:, :, P:])
+    ra = abs_v(oracle.causal_attention, *dec, scale)[:, P:] if prec == "fp8" else None
+    check(f"split-merge-{prec}", prec, go, ro[:, P:], gl, rl[:, :, P:], ref_abs_o=ra,
+          fp8_path="exact")
 
 
 def test_flash_attn_func_bf16_matches_entry_point():
@@ -293,14 +298,6 @@ def _fp8_inputs(name, B, Nq, Nk, Hq, Hkv, dqk, per_head):
     return dev, dec
 
 
-# Each probability the fast path rounds to an e4m3 code (about 8 x + const, the
-# pages' rule) is within a factor of [0.917, 1.061] of the exact one
-# (test_oracle_formats.test_lean_code_ratio_bound derives it), so a row sum of them,
-# and its log, is within ln(1/0.917) = 0.0866 of the exact one; plus the FP8 score
-# error the other LSE tests allow.
-ROUNDED_LSE_BOUND = 0.0866 + 1e-2
-
-
 @pytest.mark.parametrize("case", ["square", "chunk_tail", "mla_chunk", "q_longer"])
 def test_rounded_lse(case):
     """O is byte-identical to the lse == NULL call; the LSE is within the rounding bound
@@ -320,7 +317,7 @@ def test_rounded_lse(case):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     ro, rl = oracle.offset_attention(*dec, scale, off)
     go, gl = _host(o2, l2)
-    check(case, "fp8", go, ro)
+    check(case, "fp8", go, ro, fp8_path="lean", ref_abs_o=abs_v(oracle.offset_attention, *dec, scale, off))
     err = float(np.max(np.abs(gl - rl)))
     note(f"  rounded LSE max |error| {err:.4f} (bound {ROUNDED_LSE_BOUND:.4f})")
     assert np.all(np.isfinite(gl)) and err <= ROUNDED_LSE_BOUND
@@ -348,5 +345,6 @@ def test_rounded_lse_merge_of_split_keys():
     torch.cuda.synchronize()
     ro, rl = oracle.offset_attention(dec[0][:, P:], dec[1], dec[2], scale, P)
     go, gl = _host(om, lm)
-    check("rounded merge", "fp8", go, ro)
+    check("rounded merge", "fp8", go, ro, fp8_path="lean",
+          ref_abs_o=abs_v(oracle.offset_attention, dec[0][:, P:], dec[1], dec[2], scale, P))
     assert float(np.max(np.abs(gl - rl))) <= ROUNDED_LSE_BOUND

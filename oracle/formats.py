@@ -237,3 +237,79 @@ def quantize_e4m3_hadamard(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, n
     codes, ds = quantize_e4m3(xu, per_head)
     post = np.float32(1.0 / np.sqrt(float(hb)))
     return codes, (ds * post).astype(np.float32)
+
+
+# ---- Q/K quantisation with the large-product channels moved to the end of the row ----
+# Not on the pages.  The pages name the FP8 error of Q and K as the one that matters
+# (spke.com "ZYFAのFP8アテンションの精度はどのくらいか?"); on the device the FP8 matrix
+# instruction adds up runs of 8 channel products after aligning them to the largest one,
+# so a channel with a large Q or K magnitude swamps the small products that share its
+# run.  Permuting the channels of Q and K the same way leaves every score Q.K unchanged,
+# so the quantiser may store them in any common order: this one moves, per KV head, the
+# n_split channels with the largest product bound to the end of every Q and K row, where
+# the attention that follows can multiply them exactly.  Reading used here:
+#   * channel absmax: max |x| over all (b, n) of one head, NaN elements ignored;
+#   * importance of channel c for KV head g: fl32(max over the query heads h of g of
+#     amax_q[h, c]) * amax_k[g, c], in float32, and 0 when either factor is 0;
+#   * the n_split channels of largest importance (ties: the lower channel first) go
+#     last, in ascending channel order, after the other channels in ascending order;
+#   * codes and descales are those of quantize_e4m3 (or quantize_e4m3_q_pow2 for Q)
+#     of the unpermuted tensor, the codes then permuted: stored position j of a row of
+#     head h holds channel perm[g(h), j].
+
+OUTLIER_CHANNELS = 32
+
+
+def channel_absmax(x: np.ndarray) -> np.ndarray:
+    """(B, N, H, d) float32 -> (H, d) float32: max |x| over batch and position, NaN
+    elements taking no part (an all-NaN or all-zero channel gives 0)."""
+    a = np.abs(np.asarray(x, dtype=np.float32))
+    a = np.where(np.isnan(a), np.float32(0.0), a)
+    return np.max(a, axis=(0, 1)).astype(np.float32)
+
+
+def outlier_permutation(amax_q: np.ndarray, amax_k: np.ndarray, n_split: int) -> np.ndarray:
+    """(Hq, d), (Hkv, d) channel absmax -> (Hkv, d) int64 permutation: row g lists the
+    source channel of every stored position, the n_split channels of largest importance
+    last (see the reading above)."""
+    amax_q = np.asarray(amax_q, np.float32)
+    amax_k = np.asarray(amax_k, np.float32)
+    Hq, d = amax_q.shape
+    Hkv = amax_k.shape[0]
+    if Hq % Hkv or not 0 < n_split <= d:
+        raise ValueError("need Hq % Hkv == 0 and 0 < n_split <= d")
+    G = Hq // Hkv
+    perm = np.empty((Hkv, d), dtype=np.int64)
+    for g in range(Hkv):
+        aq = np.max(amax_q[g * G:(g + 1) * G], axis=0).astype(np.float32)
+        ak = amax_k[g]
+        with np.errstate(invalid="ignore"):      # 0 * inf, replaced by 0 below
+            prod = (aq * ak).astype(np.float32)
+        imp = np.where((aq == 0) | (ak == 0), np.float32(0.0), prod)
+        order = sorted(range(d), key=lambda c: (-float(imp[c]), c))
+        chosen = set(order[:n_split])
+        perm[g] = [c for c in range(d) if c not in chosen] + sorted(chosen)
+    return perm
+
+
+def quantize_e4m3_qk_outliers(q: np.ndarray, k: np.ndarray, per_head: bool,
+                              n_split: int = OUTLIER_CHANNELS,
+                              q_pow2_scale: float | None = None):
+    """Codes of Q (B, N, Hq, d) and K (B, N, Hkv, d) with each KV group's n_split
+    largest-product channels stored last.  Returns (q_codes, k_codes, q_descale,
+    k_descale, perm): codes uint8 in the permuted channel order, descales as
+    quantize_e4m3 gives them (Q's as quantize_e4m3_q_pow2 with softmax scale
+    q_pow2_scale when that is given), perm (Hkv, d)."""
+    q = np.asarray(q, dtype=np.float32)
+    k = np.asarray(k, dtype=np.float32)
+    Hq, Hkv = q.shape[2], k.shape[2]
+    perm = outlier_permutation(channel_absmax(q), channel_absmax(k), n_split)
+    kc, kd = quantize_e4m3(k, per_head)
+    if q_pow2_scale is None:
+        qc, qd = quantize_e4m3(q, per_head)
+    else:
+        qc, qd = quantize_e4m3_q_pow2(q, per_head, kd, q_pow2_scale)
+    G = Hq // Hkv
+    qp = np.stack([qc[:, :, h, perm[h // G]] for h in range(Hq)], axis=2)
+    kp = np.stack([kc[:, :, g, perm[g]] for g in range(Hkv)], axis=2)
+    return np.ascontiguousarray(qp), np.ascontiguousarray(kp), qd, kd, perm

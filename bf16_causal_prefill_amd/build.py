@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "merge.hip", "quantize.hip"]
+SOURCES = ["api.hip", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "merge.hip", "quantize.hip",
+           "outliers.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

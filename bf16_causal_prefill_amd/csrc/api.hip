@@ -68,8 +68,9 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_descale,
             const float* k_descale, const float* v_descale, int descale_per_head, void* o,
             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v,
-            float softmax_scale, void* stream, int lse_rounded = 0) {
+            float softmax_scale, void* stream, int lse_rounded = 0, int split = 0) {
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
+  if (st == ATTN_OK && split && d_qk != 128) st = ATTN_E_UNSUPPORTED;
   if (st == ATTN_OK && q_offset < 0) st = ATTN_E_INVAL;
   if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
   if (st == ATTN_OK && (!q_descale || !k_descale || !v_descale)) st = ATTN_E_INVAL;
@@ -83,6 +84,7 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
   p.lse_rounded = lse_rounded;
+  p.split = split;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
   return launch_status(attn::launch_attn_fwd_fp8(p, d_qk, (hipStream_t)stream));
@@ -133,6 +135,25 @@ int attn_fwd_causal_offset_fp8_rounded_lse(const uint8_t* q, const uint8_t* k, c
   if (!lse) return ATTN_E_INVAL;
   return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
                  Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream, 1);
+}
+
+int attn_fwd_causal_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                 const float* q_descale, const float* k_descale,
+                                 const float* v_descale, int descale_per_head, void* o,
+                                 float* lse, int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                                 float softmax_scale, void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
+                 N, N, 0, d_qk, d_v, softmax_scale, stream, 0, 1);
+}
+
+int attn_fwd_causal_offset_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                        const float* q_descale, const float* k_descale,
+                                        const float* v_descale, int descale_per_head, void* o,
+                                        float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                                        int q_offset, int d_qk, int d_v, float softmax_scale,
+                                        void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
+                 Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream, 0, 1);
 }
 
 int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
@@ -191,6 +212,38 @@ int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale, int B, in
 int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, int N, int H,
                            int d, int per_head, void* stream) {
   return quantize_impl(x, out, descale, B, N, H, d, per_head, 1, stream);
+}
+
+int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, uint8_t* k_out,
+                              float* q_descale, float* k_descale, uint8_t* perm,
+                              void* workspace, size_t workspace_bytes, int B, int N, int Hq,
+                              int Hkv, int d, int per_head, int q_pow2, float softmax_scale,
+                              void* stream) {
+  if (!q || !k || !q_out || !k_out || !q_descale || !k_descale || !perm || !workspace)
+    return ATTN_E_INVAL;
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
+  if (d < ATTN_OUTLIER_CHANNELS || d > 256 || (d & 3) != 0) return ATTN_E_INVAL;
+  if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
+  if (q_pow2 != 0 && q_pow2 != 1) return ATTN_E_INVAL;
+  if (q_pow2 && !(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_E_INVAL;
+  if (Hq > 65535) return ATTN_E_INVAL;
+  if ((long long)B * N * Hq * d >= kMaxElems) return ATTN_E_INVAL;
+  if (workspace_bytes < quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d))
+    return ATTN_E_INVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 4) || !aligned(k_out, 4) ||
+      !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(perm, 4) ||
+      !aligned(workspace, 4))
+    return ATTN_E_ALIGN;
+  const int st = check_device();
+  if (st != ATTN_OK) return st;
+  return launch_status(attn::launch_quantize_e4m3_qk_outliers(
+      q, k, q_out, k_out, q_descale, k_descale, perm, (uint32_t*)workspace, B, N, Hq, Hkv, d,
+      per_head, q_pow2, softmax_scale, (hipStream_t)stream));
+}
+
+size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d) {
+  if (Hq < 1 || Hkv < 1 || d < 1) return 0;
+  return (size_t)(Hq + Hkv) * (size_t)d * sizeof(uint32_t);
 }
 
 const char* attn_status_string(int status) {

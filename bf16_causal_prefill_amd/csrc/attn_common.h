@@ -128,6 +128,19 @@ __device__ __forceinline__ void keep_in_vgprs(const T& x) {
 #endif
 }
 
+// Eight e4m3 codes (bytes of lo, then hi, in order) as bf16, exactly: every e4m3 value
+// is a bf16 value (3 of bf16's 7 mantissa bits, exponents 2^-9 .. 2^8).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 __device__ __forceinline__ i32x8 load_i32x8(const char* p) {
   const uint4 a = *(const uint4*)p;
   const uint4 b = *(const uint4*)(p + 16);

@@ -37,6 +37,7 @@
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -91,9 +92,12 @@ int attn_fwd_causal_bf16(const void* q, const void* k, const void* v,
  *             a Q descale), that power of two is applied by the Q operand's
  *             scale of the matrix instruction, which then yields the exponent
  *             arguments directly (no multiply-add per score, about 8% faster).
- * The FP8 matrix instructions sum each run of 8 products after aligning them to
- * the largest, keeping about 12 bits below it, so scores carry an error of up to
- * 7 * 2^-12 * max|q_c k_c| per 8 channels; O and LSE inherit it.
+ * The FP8 matrix instructions sum each run of 8 consecutive channel products
+ * after truncating every product toward zero to a multiple of 2^(E - 13), E the
+ * largest exponent sum e_q + e_k of the run's factors (measured), so a score
+ * carries an error below 7 * 2^(E-13) per run of 8 channels; O and LSE inherit
+ * it.  On inputs with outlier channels that reaches 0.1-0.3 in the LSE: use
+ * quantize_e4m3_qk_outliers with attn_fwd_causal_fp8_outliers there.
  */
 int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
                         const float* q_descale, const float* k_descale,
@@ -245,6 +249,88 @@ int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale,
  */
 int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale,
                            int B, int N, int H, int d, int per_head, void* stream);
+
+/*
+ * Outlier channels.  gfx950's FP8 matrix instructions add each run of 8
+ * consecutive channel products after truncating every product toward zero to
+ * 13 bits below the run's largest exponent sum (measured through this library).  One
+ * channel whose Q or K magnitude is far above the others (the outlier
+ * channels of real activations) then swamps the small products of its run:
+ * on such inputs the scores, and the LSE, move by up to about 0.1-0.3 instead
+ * of the rounding of the inputs (the pages name the FP8 error of Q and K as
+ * the one that matters, spke.com "ZYFAのFP8アテンションの精度はどのくらいか?").
+ * Permuting the channels of Q and K the same way leaves every score
+ * unchanged, so the pair below takes those channels out of the FP8 products:
+ * quantize_e4m3_qk_outliers stores each KV head's ATTN_OUTLIER_CHANNELS
+ * largest-product channels last, and attn_fwd_causal_fp8_outliers multiplies
+ * the last ATTN_OUTLIER_CHANNELS channels of every Q and K row on the BF16
+ * matrix instructions (exact products of the e4m3 values, float32 sums).
+ */
+#define ATTN_OUTLIER_CHANNELS 32
+
+/*
+ * e4m3 quantisation of Q (B, N, Hq, d) and K (B, N, Hkv, d), float32, with
+ * each KV head's largest-product channels stored last in every Q and K row.
+ *   Channel absmax: max |x| over all (b, n) of one head (NaN ignored).  The
+ *   importance of channel c for KV head g is the float32 product of the
+ *   largest Q absmax of c among g's query heads and K's absmax of c (0 when
+ *   either is 0).  The ATTN_OUTLIER_CHANNELS channels of largest importance
+ *   (ties: the lower channel) are stored last in ascending channel order,
+ *   after the other channels in ascending order.
+ *   q_out, k_out  DEVICE uint8 codes (same shapes), 4-byte aligned: stored
+ *             position j of a row of head h (KV head g = h / (Hq / Hkv) for Q)
+ *             holds the code of channel perm[g * d + j]; the codes themselves
+ *             are quantize_e4m3's (x / descale rounded to nearest even).
+ *   q_descale, k_descale  DEVICE float32 outputs, Hq / Hkv values (per_head)
+ *             or 1 each: quantize_e4m3's descales; with q_pow2 = 1, Q's is
+ *             the one quantize_e4m3_q_pow2 would choose against K's.
+ *   perm      DEVICE uint8 output (Hkv, d), 4-byte aligned.
+ *   workspace DEVICE scratch of workspace_bytes >=
+ *             quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d) bytes,
+ *             4-byte aligned; its contents on entry do not matter.
+ *   q, k      DEVICE float32, 16-byte aligned.
+ *   d         a multiple of 4 in [ATTN_OUTLIER_CHANNELS, 256]; Hq % Hkv == 0;
+ *             softmax_scale finite and > 0 when q_pow2 (else unused).
+ * Codes and descales are bit-identical across runs.  Six kernels are
+ * enqueued.  Invalid arguments return ATTN_E_INVAL / ATTN_E_ALIGN before any
+ * launch.
+ */
+int quantize_e4m3_qk_outliers(const float* q, const float* k,
+                              uint8_t* q_out, uint8_t* k_out,
+                              float* q_descale, float* k_descale, uint8_t* perm,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int N, int Hq, int Hkv, int d, int per_head,
+                              int q_pow2, float softmax_scale, void* stream);
+
+/* Bytes of workspace quantize_e4m3_qk_outliers needs: (Hq + Hkv) * d * 4. */
+size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d);
+
+/*
+ * attn_fwd_causal_fp8 and attn_fwd_causal_offset_fp8 with the last
+ * ATTN_OUTLIER_CHANNELS channels of every Q and K row multiplied on the BF16
+ * matrix instructions (e4m3 values converted exactly; exact products, float32
+ * sums) instead of the FP8 ones.  Feed them the codes of
+ * quantize_e4m3_qk_outliers (any codes are valid: the result is the same
+ * attention, only its accuracy depends on where the large channels are).
+ * d_qk must be 128 (else ATTN_E_UNSUPPORTED).  lse may be NULL (then the
+ * probabilities take the fast path, as for attn_fwd_causal_fp8).  Everything
+ * else as for those entry points.  The extra matrix work is a quarter of the
+ * Q.K^T products' FP8 time per exact channel block.
+ */
+int attn_fwd_causal_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                 const float* q_descale, const float* k_descale,
+                                 const float* v_descale, int descale_per_head,
+                                 void* o, float* lse,
+                                 int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                                 float softmax_scale, void* stream);
+
+int attn_fwd_causal_offset_fp8_outliers(const uint8_t* q, const uint8_t* k,
+                                        const uint8_t* v, const float* q_descale,
+                                        const float* k_descale, const float* v_descale,
+                                        int descale_per_head, void* o, float* lse,
+                                        int B, int Hq, int Hkv, int Nq, int Nk,
+                                        int q_offset, int d_qk, int d_v,
+                                        float softmax_scale, void* stream);
 
 /* Static, NUL-terminated name of a status code; never NULL. */
 const char* attn_status_string(int status);

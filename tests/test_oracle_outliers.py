@@ -128,20 +128,49 @@ def test_codes_are_plain_codes_permuted(per_head, pow2):
 # ---- the grouped accumulation of the FP8 matrix instruction, modelled ------------------
 # Measured through the C ABI (test_gpu_parity.py, accumulation tests): each run of 8
 # consecutive channel products is added after truncating every product toward zero to
-# a multiple of 2^(E - 13), E the exponent of the run's largest product.
+# a multiple of 2^(E - 13), E the largest exponent sum e_q + e_k of the run's e4m3
+# factor pairs (subnormals count as exponent -6).
 
-def _grouped_dot(q, K):
+def _e4m3_exponent(codes):
+    e = (np.asarray(codes, np.int64) >> 3) & 0xF
+    return np.where(e == 0, -6, e - 7)
+
+
+def _grouped_dot(q, K, eq, eK):
+    """q (d,), K (M, d) e4m3 values with exponents eq, eK -> the modelled FP8 dots."""
     p = q[None, :] * K
-    pg = p.reshape(p.shape[0], -1, 8)
-    mx = np.max(np.abs(pg), axis=2, keepdims=True)
-    E = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
-    ulp = np.exp2(E - 13)
+    M, d = p.shape
+    pg = p.reshape(M, d // 8, 8)
+    es = (eq[None, :] + eK).reshape(M, d // 8, 8)
+    E = np.max(np.where(pg != 0, es, -100), axis=2, keepdims=True)
+    ulp = np.exp2(E - 13.0)
     return (np.trunc(pg / ulp) * ulp).sum(axis=(1, 2))
 
 
-def _modelled_lse_error(qv, kv, qd, kd, scale, n_exact, rows):
+def test_grouped_accumulation_model_reproduces_the_measured_cases():
+    """The model gives the scores the GPU gave in the accumulation tests."""
+    code = {1.0: 0x38, 1.5: 0x3C, 2.0: 0x40, 256.0: 0x78, 64.0: 0x68, 240.0: 0x77,
+            120.0: 0x6F, 0.5: 0x30}
+    cases = [((256, 64), (1.0, 1.0), 16384.0), ((256, 64), (1.0, -1.0), 16384.0),
+             ((256, 64), (1.5, 2.0), 16398.0), ((256, 64), (-1.5, 2.0), 16370.0),
+             ((256, 64), (2.0, 2.0), 16412.0), ((256, 64), (-0.5, 1.0), 16384.0),
+             ((240, 120), (1.5, 1.0), 28807.0)]
+    for (a0, b0), (a, b), want in cases:
+        qc = np.zeros(8, np.uint8)
+        kc = np.zeros((1, 8), np.uint8)
+        qc[0], kc[0, 0] = code[a0], code[b0]
+        qc[1:] = code[abs(a)] | (0x80 if a < 0 else 0)
+        kc[0, 1:] = code[abs(b)] | (0x80 if b < 0 else 0)
+        got = _grouped_dot(oracle.e4m3_decode(qc), oracle.e4m3_decode(kc),
+                           _e4m3_exponent(qc), _e4m3_exponent(kc))[0]
+        assert got == want, (a0, b0, a, b, got, want)
+
+
+def _modelled_lse_error(qc, kc, qd, kd, scale, n_exact, rows):
     """Worst |LSE| change over `rows` when the last n_exact stored channels are
     multiplied exactly and the rest through the modelled FP8 accumulation."""
+    qv, kv = oracle.e4m3_decode(qc), oracle.e4m3_decode(kc)
+    qe, ke = _e4m3_exponent(qc), _e4m3_exponent(kc)
     G = qv.shape[2] // kv.shape[2]
     worst = 0.0
     d = qv.shape[3]
@@ -151,7 +180,8 @@ def _modelled_lse_error(qv, kv, qd, kd, scale, n_exact, rows):
         K, q = kv[0, : i + 1, g], qv[0, i, h]
         sc = float(qd[h]) * float(kd[g]) * scale
         exact = np.logaddexp.reduce((K @ q) * sc)
-        model = _grouped_dot(np.where(split, 0.0, q), K) + K[:, split] @ q[split]
+        model = _grouped_dot(np.where(split, 0.0, q), K, qe[0, i, h], ke[0, : i + 1, g]) + \
+            K[:, split] @ q[split]
         worst = max(worst, abs(np.logaddexp.reduce(model * sc) - exact))
     return worst
 
@@ -160,11 +190,10 @@ def test_exact_channels_keep_the_lse_inside_the_gate_on_outlier_inputs():
     w = workloads.CONFIGS["mistral16k"].with_(N=512, seed=25)
     x = workloads.generate(w)
     qc, kc, qd, kd, _ = oracle.quantize_e4m3_qk_outliers(x["q"], x["k"], True)
-    qv, kv = oracle.e4m3_decode(qc), oracle.e4m3_decode(kc)
     rng = np.random.default_rng(3)
     rows = [(int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(800)]
-    plain = _modelled_lse_error(qv, kv, qd, kd, w.softmax_scale, 0, rows)
-    split = _modelled_lse_error(qv, kv, qd, kd, w.softmax_scale, oracle.OUTLIER_CHANNELS, rows)
+    plain = _modelled_lse_error(qc, kc, qd, kd, w.softmax_scale, 0, rows)
+    split = _modelled_lse_error(qc, kc, qd, kd, w.softmax_scale, oracle.OUTLIER_CHANNELS, rows)
     print(f"modelled worst LSE error: all channels FP8 {plain:.4f}, "
           f"last {oracle.OUTLIER_CHANNELS} exact {split:.5f}")
     assert plain > 1e-2

@@ -20,6 +20,7 @@ __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal
            "attn_status_string", "flash_attn_func", "quantize_e4m3_qk_outliers",
            "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
            "attn_fwd_causal_offset_fp8_outliers", "OUTLIER_CHANNELS",
+           "quantize_e4m3_qk_outliers_noalloc", "NOALLOC_SCRATCH_WORDS",
            "LIB_PATH",
            "EXPORTED_SYMBOLS"]
 
@@ -30,10 +31,13 @@ EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_fwd_causal_offset_fp8_rounded_lse", "quantize_e4m3_q_pow2",
                     "attn_status_string", "quantize_e4m3_qk_outliers",
                     "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
-                    "attn_fwd_causal_offset_fp8_outliers")
+                    "attn_fwd_causal_offset_fp8_outliers",
+                    "quantize_e4m3_qk_outliers_noalloc")
 
 # Channels per Q/K row that the *_outliers entry points multiply exactly (stored last).
 OUTLIER_CHANNELS = 32
+# 32-bit words of the fixed scratch of quantize_e4m3_qk_outliers_noalloc.
+NOALLOC_SCRATCH_WORDS = 65536
 
 ATTN_OK = 0
 ATTN_E_INVAL = -1
@@ -41,6 +45,7 @@ ATTN_E_UNSUPPORTED = -2
 ATTN_E_ALIGN = -3
 ATTN_E_NODEVICE = -4
 ATTN_E_LAUNCH = -5
+ATTN_E_TOO_LARGE = -6
 
 _lib = None
 
@@ -87,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.quantize_e4m3_qk_outliers.restype = i
     L.quantize_e4m3_qk_outliers_workspace_bytes.argtypes = [i, i, i]
     L.quantize_e4m3_qk_outliers_workspace_bytes.restype = ctypes.c_size_t
+    L.quantize_e4m3_qk_outliers_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                                    i, i, i, i, i, i, i, f, vp]
+    L.quantize_e4m3_qk_outliers_noalloc.restype = i
     L.attn_fwd_causal_fp8_outliers.argtypes = L.attn_fwd_causal_fp8.argtypes
     L.attn_fwd_causal_fp8_outliers.restype = i
     L.attn_fwd_causal_offset_fp8_outliers.argtypes = L.attn_fwd_causal_offset_fp8.argtypes
@@ -385,6 +393,39 @@ def quantize_e4m3_qk_outliers(q, k, q_out, k_out, q_descale, k_descale, perm, pe
     descale makes the FP8 softmax constant a power of two (softmax_scale, default
     1/sqrt(d)).  workspace: a device buffer of at least
     quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d) bytes (allocated here when None)."""
+    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm,
+                                           per_head)
+    _on_gpu(q.device, workspace=workspace)
+    need = quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    nbytes = int(workspace.numel() * workspace.element_size())
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = load_library().quantize_e4m3_qk_outliers(
+        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_descale), _ptr(k_descale), _ptr(perm),
+        _ptr(workspace), nbytes, B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)),
+        scale, _stream(stream))
+    _check(st, "quantize_e4m3_qk_outliers")
+
+
+def quantize_e4m3_qk_outliers_noalloc(q, k, q_out, k_out, q_descale, k_descale, perm,
+                                      per_head: bool, q_pow2: bool = False, softmax_scale=None,
+                                      stream=None) -> None:
+    """quantize_e4m3_qk_outliers with the library's fixed per-device scratch instead of a
+    workspace (nothing is allocated; (Hq + Hkv) * d <= NOALLOC_SCRATCH_WORDS; calls that
+    overlap on one GPU race)."""
+    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm,
+                                           per_head)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = load_library().quantize_e4m3_qk_outliers_noalloc(
+        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_descale), _ptr(k_descale), _ptr(perm),
+        B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)), scale, _stream(stream))
+    _check(st, "quantize_e4m3_qk_outliers_noalloc")
+
+
+def _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm, per_head):
+    """Checks of the joint quantisers' arguments; returns (B, N, Hq, Hkv, d)."""
     B, N, Hq, d = _rank4(q, "q")
     Hkv = _rank4(k, "k")[2]
     _want(q, "q", "f32", (B, N, Hq, d))
@@ -399,18 +440,8 @@ def quantize_e4m3_qk_outliers(q, k, q_out, k_out, q_descale, k_descale, perm, pe
     if Hkv < 1 or Hq % Hkv:
         raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
     _on_gpu(q.device, q=q, k=k, q_out=q_out, k_out=k_out, q_descale=q_descale,
-            k_descale=k_descale, perm=perm, workspace=workspace)
-    need = quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d)
-    if workspace is None:
-        import torch
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
-    nbytes = int(workspace.numel() * workspace.element_size())
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    st = load_library().quantize_e4m3_qk_outliers(
-        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_descale), _ptr(k_descale), _ptr(perm),
-        _ptr(workspace), nbytes, B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)),
-        scale, _stream(stream))
-    _check(st, "quantize_e4m3_qk_outliers")
+            k_descale=k_descale, perm=perm)
+    return B, N, Hq, Hkv, d
 
 
 def attn_merge_partials(o_a, lse_a, o_b, lse_b, o, lse=None, stream=None) -> None:

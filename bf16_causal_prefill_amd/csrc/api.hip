@@ -214,13 +214,12 @@ int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, 
   return quantize_impl(x, out, descale, B, N, H, d, per_head, 1, stream);
 }
 
-int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, uint8_t* k_out,
-                              float* q_descale, float* k_descale, uint8_t* perm,
-                              void* workspace, size_t workspace_bytes, int B, int N, int Hq,
-                              int Hkv, int d, int per_head, int q_pow2, float softmax_scale,
-                              void* stream) {
-  if (!q || !k || !q_out || !k_out || !q_descale || !k_descale || !perm || !workspace)
-    return ATTN_E_INVAL;
+static int quantize_e4m3_qk_outliers_check(const float* q, const float* k, uint8_t* q_out,
+                                           uint8_t* k_out, float* q_descale,
+                                           float* k_descale, uint8_t* perm, int B, int N,
+                                           int Hq, int Hkv, int d, int per_head, int q_pow2,
+                                           float softmax_scale) {
+  if (!q || !k || !q_out || !k_out || !q_descale || !k_descale || !perm) return ATTN_E_INVAL;
   if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
   if (d < ATTN_OUTLIER_CHANNELS || d > 256 || (d & 3) != 0) return ATTN_E_INVAL;
   if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
@@ -228,17 +227,53 @@ int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, ui
   if (q_pow2 && !(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_E_INVAL;
   if (Hq > 65535) return ATTN_E_INVAL;
   if ((long long)B * N * Hq * d >= kMaxElems) return ATTN_E_INVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 4) || !aligned(k_out, 4) ||
+      !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(perm, 4))
+    return ATTN_E_ALIGN;
+  return ATTN_OK;
+}
+
+int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, uint8_t* k_out,
+                              float* q_descale, float* k_descale, uint8_t* perm,
+                              void* workspace, size_t workspace_bytes, int B, int N, int Hq,
+                              int Hkv, int d, int per_head, int q_pow2, float softmax_scale,
+                              void* stream) {
+  if (!workspace) return ATTN_E_INVAL;
+  int st0 = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_descale, k_descale, perm, B,
+                                            N, Hq, Hkv, d, per_head, q_pow2, softmax_scale);
+  if (st0 != ATTN_OK) return st0;
   if (workspace_bytes < quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d))
     return ATTN_E_INVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 4) || !aligned(k_out, 4) ||
-      !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(perm, 4) ||
-      !aligned(workspace, 4))
-    return ATTN_E_ALIGN;
+  if (!aligned(workspace, 4)) return ATTN_E_ALIGN;
   const int st = check_device();
   if (st != ATTN_OK) return st;
   return launch_status(attn::launch_quantize_e4m3_qk_outliers(
       q, k, q_out, k_out, q_descale, k_descale, perm, (uint32_t*)workspace, B, N, Hq, Hkv, d,
       per_head, q_pow2, softmax_scale, (hipStream_t)stream));
+}
+
+int quantize_e4m3_qk_outliers_noalloc(const float* q, const float* k, uint8_t* q_out,
+                                      uint8_t* k_out, float* q_descale, float* k_descale,
+                                      uint8_t* perm, int B, int N, int Hq, int Hkv, int d,
+                                      int per_head, int q_pow2, float softmax_scale,
+                                      void* stream) {
+  // Every argument check before the first HIP call; the scratch address is only looked
+  // up for a call that will run (the first one on each device).
+  const int st = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_descale, k_descale,
+                                                 perm, B, N, Hq, Hkv, d, per_head, q_pow2,
+                                                 softmax_scale);
+  if (st != ATTN_OK) return st;
+  if ((long long)(Hq + Hkv) * d > (long long)ATTN_NOALLOC_SCRATCH_WORDS) return ATTN_E_TOO_LARGE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return ATTN_E_NODEVICE;
+  }
+  uint32_t* ws = attn::scratch_ptr(dev);
+  if (!ws) return ATTN_E_LAUNCH;
+  return launch_status(attn::launch_quantize_e4m3_qk_outliers(
+      q, k, q_out, k_out, q_descale, k_descale, perm, ws, B, N, Hq, Hkv, d, per_head, q_pow2,
+      softmax_scale, (hipStream_t)stream));
 }
 
 size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d) {
@@ -254,6 +289,8 @@ const char* attn_status_string(int status) {
     case ATTN_E_ALIGN: return "misaligned tensor pointer";
     case ATTN_E_NODEVICE: return "no usable HIP device";
     case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_TOO_LARGE:
+      return "(Hq + Hkv) * d exceeds the scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -52,4 +52,9 @@ hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint
                                             int Hkv, int d, int per_head, int q_pow2,
                                             float softmax_scale, hipStream_t stream);
 
+// Device address of the file-scope scratch array of quantize_e4m3_qk_outliers_noalloc on
+// `device` (which must be current), or nullptr.
+constexpr int kMaxDevices = 64;
+uint32_t* scratch_ptr(int device);
+
 }  // namespace attn

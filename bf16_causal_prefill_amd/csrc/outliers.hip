@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "kernels.h"
@@ -194,7 +195,34 @@ __global__ __launch_bounds__(QO_THREADS) void qo_encode(const float* __restrict_
   }
 }
 
+// Scratch of quantize_e4m3_qk_outliers_noalloc: the per-channel absmax accumulators,
+// (Hq + Hkv) * d words at most ATTN_NOALLOC_SCRATCH_WORDS.  One copy per device, held
+// until the process ends; host code uses the device address from hipGetSymbolAddress
+// (scratch_ptr below), never this name.
+__device__ __align__(256) uint32_t scratch[ATTN_NOALLOC_SCRATCH_WORDS];
+
 }  // namespace
+
+// Device address of this device's scratch array, looked up once per device with that
+// device current (the first call on it); nullptr if the lookup fails.
+uint32_t* scratch_ptr(int device) {
+  static std::mutex mu;
+  static uint32_t* ptrs[kMaxDevices] = {};
+  static bool done[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;          // not cached: a later call may retry
+    }
+    ptrs[device] = (uint32_t*)p;
+    done[device] = true;
+  }
+  return ptrs[device];
+}
 
 hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out,
                                             uint8_t* k_out, float* q_descale,

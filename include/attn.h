@@ -50,8 +50,10 @@ enum attn_status {
   ATTN_E_UNSUPPORTED = -2,  /* (d_qk, d_v) not one of the supported pairs      */
   ATTN_E_ALIGN = -3,        /* a tensor pointer is not 16-byte aligned         */
   ATTN_E_NODEVICE = -4,     /* no usable HIP device                            */
-  ATTN_E_LAUNCH = -5        /* the HIP runtime reported a launch error (this
+  ATTN_E_LAUNCH = -5,       /* the HIP runtime reported a launch error (this
                                includes a device without gfx950 code)          */
+  ATTN_E_TOO_LARGE = -6     /* sizes beyond the fixed scratch of an
+                               allocation-free entry point                     */
 };
 
 /*
@@ -304,6 +306,29 @@ int quantize_e4m3_qk_outliers(const float* q, const float* k,
 
 /* Bytes of workspace quantize_e4m3_qk_outliers needs: (Hq + Hkv) * d * 4. */
 size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d);
+
+/*
+ * quantize_e4m3_qk_outliers without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the per-channel accumulators live in
+ * a fixed scratch array of ATTN_NOALLOC_SCRATCH_WORDS 32-bit words per device,
+ * part of the library's device code (each GPU the library runs on holds its own
+ * copy, 256 KiB, until the process ends).  The call allocates nothing.
+ *   (Hq + Hkv) * d > ATTN_NOALLOC_SCRATCH_WORDS returns ATTN_E_TOO_LARGE before
+ *   any launch; other arguments, results and errors as for
+ *   quantize_e4m3_qk_outliers (bit-identical outputs).
+ *   The scratch is cleared by the call's first kernel, so earlier calls leave
+ *   nothing behind that matters; but every call on one GPU shares it, so calls
+ *   that overlap on one GPU (other streams, other threads) race and give wrong
+ *   results: serialise them.  The first call on each device looks the array's
+ *   address up (hipGetSymbolAddress) and keeps it.
+ */
+#define ATTN_NOALLOC_SCRATCH_WORDS 65536
+int quantize_e4m3_qk_outliers_noalloc(const float* q, const float* k,
+                                      uint8_t* q_out, uint8_t* k_out,
+                                      float* q_descale, float* k_descale, uint8_t* perm,
+                                      int B, int N, int Hq, int Hkv, int d, int per_head,
+                                      int q_pow2, float softmax_scale, void* stream);
 
 /*
  * attn_fwd_causal_fp8 and attn_fwd_causal_offset_fp8 with the last

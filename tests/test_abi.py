@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = ba.attn_status_string(code)
         assert s and s != "unknown status"
     assert ba.attn_status_string(12345) == "unknown status"
@@ -321,3 +321,28 @@ def test_binding_rejects_outlier_quantiser_mismatch(no_library):
         ba.quantize_e4m3_qk_outliers(**dict(a, k_out=_t((1, 4, 4, 128), torch.uint8)))
     with pytest.raises(ValueError, match="GPU tensor"):
         ba.quantize_e4m3_qk_outliers(**a)
+
+
+def test_noalloc_quantiser_validates_and_bounds_its_scratch():
+    """quantize_e4m3_qk_outliers_noalloc: the same argument checks as the workspace
+    form, and (Hq + Hkv) * d beyond its fixed scratch is ATTN_E_TOO_LARGE, all before
+    any HIP call."""
+    lib = ba.load_library()
+    vp = ctypes.c_void_p
+
+    def qz(B=1, N=4, Hq=4, Hkv=2, d=128, ph=1, p2=0, s=0.1, q=A16, perm=A16):
+        return lib.quantize_e4m3_qk_outliers_noalloc(vp(q), vp(A16), vp(A16), vp(A16), vp(A16),
+                                                     vp(A16), vp(perm), B, N, Hq, Hkv, d, ph,
+                                                     p2, ctypes.c_float(s), None)
+    assert qz(q=None) == ba.ATTN_E_INVAL
+    assert qz(Hq=3) == ba.ATTN_E_INVAL
+    assert qz(d=28) == ba.ATTN_E_INVAL
+    assert qz(p2=1, s=float("nan")) == ba.ATTN_E_INVAL
+    assert qz(perm=A16 + 1) == ba.ATTN_E_ALIGN
+    words = ba.NOALLOC_SCRATCH_WORDS
+    assert qz(Hq=words // 128, Hkv=words // 128, d=128) == ba.ATTN_E_TOO_LARGE
+    assert qz(Hq=256, Hkv=4, d=256) == ba.ATTN_E_TOO_LARGE       # 260 * 256 > 65536
+    assert "scratch" in ba.attn_status_string(ba.ATTN_E_TOO_LARGE)
+    if _no_device():
+        assert qz() == ba.ATTN_E_NODEVICE
+        assert qz(Hq=256, Hkv=256, d=128) == ba.ATTN_E_NODEVICE   # exactly at the limit

@@ -183,6 +183,102 @@ def energy_of(fn, flops: float, read, seconds: float = 3.0, clock=None) -> dict:
             "sclk_mhz": round(sum(clk) / len(clk), 1) if clk else None}
 
 
+def timed_with_clock(fn, flops: float, clock=None, seconds: float = 1.0, iters: int = 30):
+    """Kernel-only rate of fn: about 0.3 s of back-to-back calls to settle the clock, then
+    `iters` calls timed with HIP events on the current stream while a host thread polls
+    the shader clock every 5 ms; returns (ms, TFLOP/s, mean SCLK in MHz or None)."""
+    import torch
+    t_ms = time_events(fn, 3)
+    for _ in range(max(2, int(300.0 / max(t_ms, 1e-3)))):
+        fn()
+    torch.cuda.synchronize()
+    n = max(iters, int(seconds * 1e3 / max(t_ms, 1e-3)))
+    clk, stop = [], threading.Event()
+
+    def poll():
+        while not stop.wait(0.005):
+            c = clock()
+            if c is not None:
+                clk.append(c)
+    poller = threading.Thread(target=poll, daemon=True) if clock is not None else None
+    if poller is not None:
+        poller.start()
+    ms = time_events(fn, n, warmup=0)
+    if poller is not None:
+        stop.set()
+        poller.join()
+    return ms, flops / ms / 1e9, (round(sum(clk) / len(clk), 1) if clk else None)
+
+
+def config_lines(ba, torch, name: str, clock) -> dict:
+    """Kernel-only TFLOP/s, % of the dense peak and sustained SCLK of the attention
+    kernels on one workload: FP8 with the LSE (Q quantised for the power-of-two softmax
+    constant, and with its absmax scale), FP8 without the LSE, BF16 with the LSE; on the
+    outlier-channel recipe also the exact-channel kernel on the joint Q/K quantiser's
+    codes (the path that meets the LSE gate there) and that quantiser's time."""
+    import workloads
+    w = workloads.get(name)
+    x = workloads.generate(w)
+    dev = "cuda:0"
+    xd = {n: torch.from_numpy(x[n]).to(dev) for n in "qkv"}
+    nds = lambda H: (H if w.fp8_per_head else 1)
+    codes = {n: torch.empty(x[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
+    ds = {"q": torch.empty(nds(w.Hq), device=dev), "k": torch.empty(nds(w.Hkv), device=dev),
+          "v": torch.empty(nds(w.Hkv), device=dev)}
+    o = torch.empty((w.B, w.N, w.Hq, w.d_v), device=dev, dtype=torch.bfloat16)
+    lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
+    flops = workloads.causal_flops(w)
+    ph = int(w.fp8_per_head)
+    out = {}
+
+    def put(tag, fn, prec):
+        ms, tf, clk = timed_with_clock(fn, flops, clock)
+        out[tag + "_tflops"] = round(tf, 1)
+        out[tag + "_pct_peak"] = round(100.0 * tf / PEAK_TFLOPS[prec], 2)
+        out[tag + "_sclk_mhz"] = clk
+
+    for n in "kv":
+        ba.quantize_e4m3(xd[n], codes[n], ds[n], per_head=w.fp8_per_head)
+    ba.quantize_e4m3(xd["q"], codes["q"], ds["q"], per_head=w.fp8_per_head)
+    fp8 = lambda L: (lambda: ba.attn_fwd_causal_fp8(
+        codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], o, L,
+        softmax_scale=w.softmax_scale, descale_per_head=ph))
+    put("fp8_lse_absmax_q", fp8(lse), "fp8")
+    put("fp8_nolse", fp8(None), "fp8")
+    ba.quantize_e4m3_q_pow2(xd["q"], codes["q"], ds["q"], ds["k"], w.softmax_scale,
+                            per_head=w.fp8_per_head)
+    put("fp8_lse", fp8(lse), "fp8")
+    if w.d_qk == 128:
+        # the exact-channel kernel (32 channels on the BF16 pipe), on the joint quantiser's
+        # codes with the power-of-two Q scale
+        perm = torch.empty((w.Hkv, w.d_qk), device=dev, dtype=torch.uint8)
+        T = ba.OUTLIER_CHANNELS
+        qx = torch.empty((w.B, w.N, w.Hq, T), device=dev, dtype=torch.bfloat16)
+        kx = torch.empty((w.B, w.N, w.Hkv, T), device=dev, dtype=torch.bfloat16)
+        wsb = torch.empty(ba.quantize_e4m3_qk_outliers_workspace_bytes(w.Hq, w.Hkv, w.d_qk),
+                          device=dev, dtype=torch.uint8)
+        quant_o = lambda: ba.quantize_e4m3_qk_outliers(
+            xd["q"], xd["k"], codes["q"], codes["k"], qx, kx, ds["q"], ds["k"], perm,
+            w.fp8_per_head, q_pow2=True, softmax_scale=w.softmax_scale, workspace=wsb)
+        t = time_events(quant_o, 10)
+        # 2 reads + code write + the side arrays (32 of d channels as bf16)
+        qbytes = sum(x[n].nbytes * 2 + x[n].size + x[n].size * 2 * T // w.d_qk for n in "qk")
+        out["quantize_qk_outliers_ms"] = round(t, 4)
+        out["quantize_qk_outliers_GBps"] = round(qbytes / t / 1e6, 1)
+        quant_o()
+        fo = lambda L: (lambda: ba.attn_fwd_causal_fp8_outliers(
+            codes["q"], codes["k"], codes["v"], qx, kx, ds["q"], ds["k"], ds["v"], o, L,
+            softmax_scale=w.softmax_scale, descale_per_head=ph))
+        put("fp8_outliers_lse", fo(lse), "fp8")
+        put("fp8_outliers_nolse", fo(None), "fp8")
+    del codes
+    xb = {n: xd[n].to(torch.bfloat16) for n in "qkv"}
+    del xd
+    put("bf16_lse", lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, lse,
+                                                    softmax_scale=w.softmax_scale), "bf16")
+    return out
+
+
 def cpu_baseline(w, x, n_heads: int):
     """The fp64 oracle on query heads 0..n_heads-1 (all N rows) of the workload's
     e4m3-decoded inputs (per-tensor descales from the whole tensors).  Only the
@@ -436,29 +532,16 @@ def main() -> int:
                 "source": "amdsmi energy counter of the GPU (whole device), gauss32k"}
         del xb
         extra.update(beyond_pages(ba, torch, w, xd, codes, ds, quant))
-        wm = workloads.get("mla32k")
-        log("bench: generating mla32k inputs")
-        xm = workloads.generate(wm)
-        xmd = {n: torch.from_numpy(xm[n]).to(dev) for n in "qkv"}
-        om = torch.empty((wm.B, wm.N, wm.Hq, wm.d_v), device=dev, dtype=torch.bfloat16)
-        lm = torch.empty((wm.B, wm.Hq, wm.N), device=dev, dtype=torch.float32)
-        fm = workloads.causal_flops(wm)
-        cm = {n: torch.empty(xm[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
-        dm = {n: torch.empty(xm[n].shape[2], device=dev) for n in "qkv"}
-        for n in "kv":
-            ba.quantize_e4m3(xmd[n], cm[n], dm[n], per_head=True)
-        ba.quantize_e4m3_q_pow2(xmd["q"], cm["q"], dm["q"], dm["k"], wm.softmax_scale,
-                                per_head=True)
-        for tag, L in (("mla32k_fp8_attn_lse", lm), ("mla32k_fp8_attn_nolse", None)):
-            t = time_events(lambda: ba.attn_fwd_causal_fp8(
-                cm["q"], cm["k"], cm["v"], dm["q"], dm["k"], dm["v"], om, L,
-                softmax_scale=wm.softmax_scale, descale_per_head=1), 10)
-            extra[tag + "_tflops"] = round(fm / t / 1e9, 1)
-        xmb = {n: xmd[n].to(torch.bfloat16) for n in "qkv"}
-        t = time_events(lambda: ba.attn_fwd_causal_bf16(xmb["q"], xmb["k"], xmb["v"], om, lm,
-                                                        softmax_scale=wm.softmax_scale), 10)
-        extra["mla32k_bf16_attn_lse_tflops"] = round(fm / t / 1e9, 1)
-        del xmd, xmb, cm
+        # kernel-only lines with sustained clock for every workload of the metric
+        clock = gpu_clock_reader()
+        extra["configs"] = {}
+        for cname in ("mid_gqa", "mistral16k", "mla16k", "mla32k"):
+            log(f"bench: kernel lines on {cname}")
+            extra["configs"][cname] = config_lines(ba, torch, cname, clock)
+        # the same lines on the headline workload (the exact-channel kernel's cost on
+        # inputs without outlier channels, next to the plain kernel's)
+        log("bench: kernel lines on gauss32k")
+        extra["configs"]["gauss32k"] = config_lines(ba, torch, "gauss32k", clock)
 
     cpu = None
     if not args.no_cpu:

@@ -87,17 +87,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.quantize_e4m3.restype = i
     L.quantize_e4m3_hadamard.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     L.quantize_e4m3_hadamard.restype = i
-    L.quantize_e4m3_qk_outliers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                            i, i, i, i, i, i, i, f, vp]
+    L.quantize_e4m3_qk_outliers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.c_size_t, i, i, i, i, i, i, i, f, vp]
     L.quantize_e4m3_qk_outliers.restype = i
     L.quantize_e4m3_qk_outliers_workspace_bytes.argtypes = [i, i, i]
     L.quantize_e4m3_qk_outliers_workspace_bytes.restype = ctypes.c_size_t
-    L.quantize_e4m3_qk_outliers_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+    L.quantize_e4m3_qk_outliers_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                     i, i, i, i, i, i, i, f, vp]
     L.quantize_e4m3_qk_outliers_noalloc.restype = i
-    L.attn_fwd_causal_fp8_outliers.argtypes = L.attn_fwd_causal_fp8.argtypes
+    L.attn_fwd_causal_fp8_outliers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp,
+                                               i, i, i, i, i, i, f, vp]
     L.attn_fwd_causal_fp8_outliers.restype = i
-    L.attn_fwd_causal_offset_fp8_outliers.argtypes = L.attn_fwd_causal_offset_fp8.argtypes
+    L.attn_fwd_causal_offset_fp8_outliers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp,
+                                                      vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_causal_offset_fp8_outliers.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -345,36 +347,49 @@ def attn_fwd_causal_offset_fp8_rounded_lse(q, k, v, q_descale, k_descale, v_desc
     _check(st, "attn_fwd_causal_offset_fp8_rounded_lse")
 
 
-def attn_fwd_causal_fp8_outliers(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
-                                 softmax_scale=None, descale_per_head=None, stream=None) -> None:
+def _exact_args(q_exact, k_exact, B, Nq, Nk, Hq, Hkv):
+    _want(q_exact, "q_exact", "bf16", (B, Nq, Hq, OUTLIER_CHANNELS))
+    _want(k_exact, "k_exact", "bf16", (B, Nk, Hkv, OUTLIER_CHANNELS))
+
+
+def attn_fwd_causal_fp8_outliers(q, k, v, q_exact, k_exact, q_descale, k_descale, v_descale, o,
+                                 lse=None, softmax_scale=None, descale_per_head=None,
+                                 stream=None) -> None:
     """attn_fwd_causal_fp8 with the last OUTLIER_CHANNELS channels of every Q and K row
-    multiplied exactly (for codes from quantize_e4m3_qk_outliers); d_qk must be 128."""
+    taken from the bf16 side arrays q_exact (B,N,Hq,32) / k_exact (B,N,Hkv,32) and
+    multiplied exactly (the outputs of quantize_e4m3_qk_outliers); d_qk must be 128."""
     B, Hq, Hkv, N, _, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=True)
     _outputs(o, lse, B, N, Hq, dv)
+    _exact_args(q_exact, k_exact, B, N, N, Hq, Hkv)
     descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
     _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
-            v_descale=v_descale)
+            v_descale=v_descale, q_exact=q_exact, k_exact=k_exact)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_fwd_causal_fp8_outliers(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_exact), _ptr(k_exact),
+        _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, N, dqk, dv, scale,
         _stream(stream))
     _check(st, "attn_fwd_causal_fp8_outliers")
 
 
-def attn_fwd_causal_offset_fp8_outliers(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
-                                        q_offset=None, softmax_scale=None,
-                                        descale_per_head=None, stream=None) -> None:
-    """attn_fwd_causal_offset_fp8 with the exact channels of attn_fwd_causal_fp8_outliers."""
+def attn_fwd_causal_offset_fp8_outliers(q, k, v, q_exact, k_exact, q_descale, k_descale,
+                                        v_descale, o, lse=None, q_offset=None,
+                                        softmax_scale=None, descale_per_head=None,
+                                        stream=None) -> None:
+    """attn_fwd_causal_offset_fp8 with the exact channels of attn_fwd_causal_fp8_outliers
+    (q_exact (B,Nq,Hq,32), k_exact (B,Nk,Hkv,32))."""
     B, Hq, Hkv, Nq, Nk, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=False)
     _outputs(o, lse, B, Nq, Hq, dv)
+    _exact_args(q_exact, k_exact, B, Nq, Nk, Hq, Hkv)
     descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
     _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
-            v_descale=v_descale)
+            v_descale=v_descale, q_exact=q_exact, k_exact=k_exact)
     off = Nk - Nq if q_offset is None else int(q_offset)
     scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_fwd_causal_offset_fp8_outliers(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_exact), _ptr(k_exact),
+        _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
         int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, off, dqk, dv, scale,
         _stream(stream))
     _check(st, "attn_fwd_causal_offset_fp8_outliers")
@@ -384,17 +399,18 @@ def quantize_e4m3_qk_outliers_workspace_bytes(Hq: int, Hkv: int, d: int) -> int:
     return int(load_library().quantize_e4m3_qk_outliers_workspace_bytes(int(Hq), int(Hkv), int(d)))
 
 
-def quantize_e4m3_qk_outliers(q, k, q_out, k_out, q_descale, k_descale, perm, per_head: bool,
-                              q_pow2: bool = False, softmax_scale=None, workspace=None,
-                              stream=None) -> None:
+def quantize_e4m3_qk_outliers(q, k, q_out, k_out, q_exact, k_exact, q_descale, k_descale, perm,
+                              per_head: bool, q_pow2: bool = False, softmax_scale=None,
+                              workspace=None, stream=None) -> None:
     """Joint e4m3 quantisation of q (B,N,Hq,d) and k (B,N,Hkv,d) float32 with each KV head's
     OUTLIER_CHANNELS largest-product channels stored last: q_out/k_out uint8 codes,
-    q_descale (Hq,)/(1,), k_descale (Hkv,)/(1,), perm uint8 (Hkv, d).  With q_pow2, Q's
+    q_exact (B,N,Hq,32) / k_exact (B,N,Hkv,32) bf16 side arrays of those last channels
+    (x / descale), q_descale (Hq,)/(1,), k_descale (Hkv,)/(1,), perm uint8 (Hkv, d).  With q_pow2, Q's
     descale makes the FP8 softmax constant a power of two (softmax_scale, default
     1/sqrt(d)).  workspace: a device buffer of at least
     quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d) bytes (allocated here when None)."""
-    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm,
-                                           per_head)
+    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_exact, k_exact, q_descale,
+                                           k_descale, perm, per_head)
     _on_gpu(q.device, workspace=workspace)
     need = quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d)
     if workspace is None:
@@ -403,28 +419,30 @@ def quantize_e4m3_qk_outliers(q, k, q_out, k_out, q_descale, k_descale, perm, pe
     nbytes = int(workspace.numel() * workspace.element_size())
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     st = load_library().quantize_e4m3_qk_outliers(
-        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_descale), _ptr(k_descale), _ptr(perm),
-        _ptr(workspace), nbytes, B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)),
+        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_exact), _ptr(k_exact),
+        _ptr(q_descale), _ptr(k_descale), _ptr(perm), _ptr(workspace), nbytes, B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)),
         scale, _stream(stream))
     _check(st, "quantize_e4m3_qk_outliers")
 
 
-def quantize_e4m3_qk_outliers_noalloc(q, k, q_out, k_out, q_descale, k_descale, perm,
-                                      per_head: bool, q_pow2: bool = False, softmax_scale=None,
-                                      stream=None) -> None:
+def quantize_e4m3_qk_outliers_noalloc(q, k, q_out, k_out, q_exact, k_exact, q_descale,
+                                      k_descale, perm, per_head: bool, q_pow2: bool = False,
+                                      softmax_scale=None, stream=None) -> None:
     """quantize_e4m3_qk_outliers with the library's fixed per-device scratch instead of a
     workspace (nothing is allocated; (Hq + Hkv) * d <= NOALLOC_SCRATCH_WORDS; calls that
     overlap on one GPU race)."""
-    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm,
-                                           per_head)
+    B, N, Hq, Hkv, d = _outlier_quant_args(q, k, q_out, k_out, q_exact, k_exact, q_descale,
+                                           k_descale, perm, per_head)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     st = load_library().quantize_e4m3_qk_outliers_noalloc(
-        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_descale), _ptr(k_descale), _ptr(perm),
+        _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_exact), _ptr(k_exact),
+        _ptr(q_descale), _ptr(k_descale), _ptr(perm),
         B, N, Hq, Hkv, d, int(bool(per_head)), int(bool(q_pow2)), scale, _stream(stream))
     _check(st, "quantize_e4m3_qk_outliers_noalloc")
 
 
-def _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm, per_head):
+def _outlier_quant_args(q, k, q_out, k_out, q_exact, k_exact, q_descale, k_descale, perm,
+                        per_head):
     """Checks of the joint quantisers' arguments; returns (B, N, Hq, Hkv, d)."""
     B, N, Hq, d = _rank4(q, "q")
     Hkv = _rank4(k, "k")[2]
@@ -432,6 +450,7 @@ def _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm, per_head
     _want(k, "k", "f32", (B, N, Hkv, d))
     _want(q_out, "q_out", "e4m3", (B, N, Hq, d))
     _want(k_out, "k_out", "e4m3", (B, N, Hkv, d))
+    _exact_args(q_exact, k_exact, B, N, N, Hq, Hkv)
     _want(q_descale, "q_descale", "f32", (Hq if per_head else 1,))
     _want(k_descale, "k_descale", "f32", (Hkv if per_head else 1,))
     if perm is None or getattr(perm, "dtype", None) is None or str(perm.dtype) != "torch.uint8" \
@@ -439,8 +458,8 @@ def _outlier_quant_args(q, k, q_out, k_out, q_descale, k_descale, perm, per_head
         raise ValueError(f"perm must be a uint8 tensor of shape {(Hkv, d)}")
     if Hkv < 1 or Hq % Hkv:
         raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
-    _on_gpu(q.device, q=q, k=k, q_out=q_out, k_out=k_out, q_descale=q_descale,
-            k_descale=k_descale, perm=perm)
+    _on_gpu(q.device, q=q, k=k, q_out=q_out, k_out=k_out, q_exact=q_exact, k_exact=k_exact,
+            q_descale=q_descale, k_descale=k_descale, perm=perm)
     return B, N, Hq, Hkv, d
 
 

@@ -68,9 +68,13 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_descale,
             const float* k_descale, const float* v_descale, int descale_per_head, void* o,
             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v,
-            float softmax_scale, void* stream, int lse_rounded = 0, int split = 0) {
+            float softmax_scale, void* stream, int lse_rounded = 0, int split = 0,
+            const void* q_exact = nullptr, const void* k_exact = nullptr) {
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
   if (st == ATTN_OK && split && d_qk != 128) st = ATTN_E_UNSUPPORTED;
+  if (st == ATTN_OK && split && (!q_exact || !k_exact)) st = ATTN_E_INVAL;
+  if (st == ATTN_OK && split && (!aligned(q_exact, 16) || !aligned(k_exact, 16)))
+    st = ATTN_E_ALIGN;
   if (st == ATTN_OK && q_offset < 0) st = ATTN_E_INVAL;
   if (st == ATTN_OK) st = check_tensors(q, k, v, o, lse);
   if (st == ATTN_OK && (!q_descale || !k_descale || !v_descale)) st = ATTN_E_INVAL;
@@ -85,6 +89,8 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   p.qds = q_descale; p.kds = k_descale; p.vds = v_descale; p.per_head = descale_per_head;
   p.lse_rounded = lse_rounded;
   p.split = split;
+  p.q_exact = q_exact;
+  p.k_exact = k_exact;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
   return launch_status(attn::launch_attn_fwd_fp8(p, d_qk, (hipStream_t)stream));
@@ -138,22 +144,24 @@ int attn_fwd_causal_offset_fp8_rounded_lse(const uint8_t* q, const uint8_t* k, c
 }
 
 int attn_fwd_causal_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                 const void* q_exact, const void* k_exact,
                                  const float* q_descale, const float* k_descale,
                                  const float* v_descale, int descale_per_head, void* o,
                                  float* lse, int B, int Hq, int Hkv, int N, int d_qk, int d_v,
                                  float softmax_scale, void* stream) {
   return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
-                 N, N, 0, d_qk, d_v, softmax_scale, stream, 0, 1);
+                 N, N, 0, d_qk, d_v, softmax_scale, stream, 0, 1, q_exact, k_exact);
 }
 
 int attn_fwd_causal_offset_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                        const void* q_exact, const void* k_exact,
                                         const float* q_descale, const float* k_descale,
                                         const float* v_descale, int descale_per_head, void* o,
                                         float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
                                         int q_offset, int d_qk, int d_v, float softmax_scale,
                                         void* stream) {
   return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
-                 Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream, 0, 1);
+                 Nq, Nk, q_offset, d_qk, d_v, softmax_scale, stream, 0, 1, q_exact, k_exact);
 }
 
 int attn_merge_partials(const void* o_a, const float* lse_a, const void* o_b,
@@ -215,11 +223,12 @@ int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, 
 }
 
 static int quantize_e4m3_qk_outliers_check(const float* q, const float* k, uint8_t* q_out,
-                                           uint8_t* k_out, float* q_descale,
-                                           float* k_descale, uint8_t* perm, int B, int N,
-                                           int Hq, int Hkv, int d, int per_head, int q_pow2,
-                                           float softmax_scale) {
-  if (!q || !k || !q_out || !k_out || !q_descale || !k_descale || !perm) return ATTN_E_INVAL;
+                                           uint8_t* k_out, void* q_exact, void* k_exact,
+                                           float* q_descale, float* k_descale, uint8_t* perm,
+                                           int B, int N, int Hq, int Hkv, int d, int per_head,
+                                           int q_pow2, float softmax_scale) {
+  if (!q || !k || !q_out || !k_out || !q_exact || !k_exact || !q_descale || !k_descale || !perm)
+    return ATTN_E_INVAL;
   if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_E_INVAL;
   if (d < ATTN_OUTLIER_CHANNELS || d > 256 || (d & 3) != 0) return ATTN_E_INVAL;
   if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
@@ -228,19 +237,21 @@ static int quantize_e4m3_qk_outliers_check(const float* q, const float* k, uint8
   if (Hq > 65535) return ATTN_E_INVAL;
   if ((long long)B * N * Hq * d >= kMaxElems) return ATTN_E_INVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 4) || !aligned(k_out, 4) ||
-      !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(perm, 4))
+      !aligned(q_exact, 16) || !aligned(k_exact, 16) || !aligned(q_descale, 4) ||
+      !aligned(k_descale, 4) || !aligned(perm, 4))
     return ATTN_E_ALIGN;
   return ATTN_OK;
 }
 
 int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, uint8_t* k_out,
-                              float* q_descale, float* k_descale, uint8_t* perm,
-                              void* workspace, size_t workspace_bytes, int B, int N, int Hq,
-                              int Hkv, int d, int per_head, int q_pow2, float softmax_scale,
-                              void* stream) {
+                              void* q_exact, void* k_exact, float* q_descale, float* k_descale,
+                              uint8_t* perm, void* workspace, size_t workspace_bytes, int B,
+                              int N, int Hq, int Hkv, int d, int per_head, int q_pow2,
+                              float softmax_scale, void* stream) {
   if (!workspace) return ATTN_E_INVAL;
-  int st0 = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_descale, k_descale, perm, B,
-                                            N, Hq, Hkv, d, per_head, q_pow2, softmax_scale);
+  int st0 = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_exact, k_exact, q_descale,
+                                            k_descale, perm, B, N, Hq, Hkv, d, per_head, q_pow2,
+                                            softmax_scale);
   if (st0 != ATTN_OK) return st0;
   if (workspace_bytes < quantize_e4m3_qk_outliers_workspace_bytes(Hq, Hkv, d))
     return ATTN_E_INVAL;
@@ -248,20 +259,20 @@ int quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out, ui
   const int st = check_device();
   if (st != ATTN_OK) return st;
   return launch_status(attn::launch_quantize_e4m3_qk_outliers(
-      q, k, q_out, k_out, q_descale, k_descale, perm, (uint32_t*)workspace, B, N, Hq, Hkv, d,
-      per_head, q_pow2, softmax_scale, (hipStream_t)stream));
+      q, k, q_out, k_out, q_exact, k_exact, q_descale, k_descale, perm, (uint32_t*)workspace, B,
+      N, Hq, Hkv, d, per_head, q_pow2, softmax_scale, (hipStream_t)stream));
 }
 
 int quantize_e4m3_qk_outliers_noalloc(const float* q, const float* k, uint8_t* q_out,
-                                      uint8_t* k_out, float* q_descale, float* k_descale,
-                                      uint8_t* perm, int B, int N, int Hq, int Hkv, int d,
-                                      int per_head, int q_pow2, float softmax_scale,
-                                      void* stream) {
+                                      uint8_t* k_out, void* q_exact, void* k_exact,
+                                      float* q_descale, float* k_descale, uint8_t* perm, int B,
+                                      int N, int Hq, int Hkv, int d, int per_head, int q_pow2,
+                                      float softmax_scale, void* stream) {
   // Every argument check before the first HIP call; the scratch address is only looked
   // up for a call that will run (the first one on each device).
-  const int st = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_descale, k_descale,
-                                                 perm, B, N, Hq, Hkv, d, per_head, q_pow2,
-                                                 softmax_scale);
+  const int st = quantize_e4m3_qk_outliers_check(q, k, q_out, k_out, q_exact, k_exact,
+                                                 q_descale, k_descale, perm, B, N, Hq, Hkv, d,
+                                                 per_head, q_pow2, softmax_scale);
   if (st != ATTN_OK) return st;
   if ((long long)(Hq + Hkv) * d > (long long)ATTN_NOALLOC_SCRATCH_WORDS) return ATTN_E_TOO_LARGE;
   int dev = -1;
@@ -272,8 +283,8 @@ int quantize_e4m3_qk_outliers_noalloc(const float* q, const float* k, uint8_t* q
   uint32_t* ws = attn::scratch_ptr(dev);
   if (!ws) return ATTN_E_LAUNCH;
   return launch_status(attn::launch_quantize_e4m3_qk_outliers(
-      q, k, q_out, k_out, q_descale, k_descale, perm, ws, B, N, Hq, Hkv, d, per_head, q_pow2,
-      softmax_scale, (hipStream_t)stream));
+      q, k, q_out, k_out, q_exact, k_exact, q_descale, k_descale, perm, ws, B, N, Hq, Hkv, d,
+      per_head, q_pow2, softmax_scale, (hipStream_t)stream));
 }
 
 size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d) {

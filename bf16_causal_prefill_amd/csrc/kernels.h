@@ -21,7 +21,9 @@ struct FwdParams {
   float scale;
   int n_qtiles;        // filled in by the launcher
   int lse_rounded;     // FP8: lse from the rounded-probability row sums (consistent with O)
-  int split;           // FP8, d_qk 128: the last 32 channels of Q and K on the BF16 pipe
+  int split;           // FP8, d_qk 128: the last 32 channels of Q and K on the BF16 pipe,
+  const void* q_exact; // from these bf16 side arrays (B, Nq, Hq, 32) and (B, Nk, Hkv, 32)
+  const void* k_exact;
 };
 
 // Enqueue the causal forward kernel (d_qk 128 or 192; d_v is 128 for both shapes).
@@ -46,8 +48,8 @@ hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* desc
 // Enqueues the joint Q/K quantisation that stores each KV head's largest-product
 // channels last (workspace: (Hq + Hkv) * d uint32 accumulators).
 hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out,
-                                            uint8_t* k_out, float* q_descale,
-                                            float* k_descale, uint8_t* perm,
+                                            uint8_t* k_out, void* q_exact, void* k_exact,
+                                            float* q_descale, float* k_descale, uint8_t* perm,
                                             uint32_t* workspace, int B, int N, int Hq,
                                             int Hkv, int d, int per_head, int q_pow2,
                                             float softmax_scale, hipStream_t stream);

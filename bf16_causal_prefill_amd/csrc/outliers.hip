@@ -18,7 +18,10 @@
 //   the ATTN_OUTLIER_CHANNELS channels of largest importance (ties: the lower channel)
 //   are stored last, in ascending channel order, after the others in ascending order;
 //   codes and descales are exactly quantize_e4m3's (Q's descale optionally
-//   quantize_e4m3_q_pow2's), only the channel order changes.
+//   quantize_e4m3_q_pow2's), only the channel order changes;
+//   the last ATTN_OUTLIER_CHANNELS stored channels are also written as bf16 side arrays
+//   (round to nearest even of the float32 quotient x / descale), which the exact-channel
+//   attention multiplies on the BF16 matrix pipe instead of the codes.
 //
 // Kernels, in stream order:
 //   1. clear    the per-channel absmax accumulators in the workspace
@@ -166,12 +169,21 @@ __global__ __launch_bounds__(QO_THREADS) void qo_select(const uint32_t* amax_q,
   }
 }
 
+// bf16 bits of a float32, round to nearest even (overflow to infinity), NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Stored word w of every row (4 channels): word w of row r belongs to head
 // h = w / d4 at stored channels 4(w % d4) .. +3, which hold source channels
 // perm[(h / G) * d + ...].  The gathered values are divided by the head's descale and
-// encoded as in quantize_e4m3.
+// encoded as in quantize_e4m3; words of the last ATTN_OUTLIER_CHANNELS stored channels
+// also write the bf16 quotients into the side array exact (rows of H * 32 values).
 __global__ __launch_bounds__(QO_THREADS) void qo_encode(const float* __restrict__ x,
                                                        uint32_t* __restrict__ out,
+                                                       uint2* __restrict__ exact,
                                                        const float* descale,
                                                        const uint8_t* perm, long long words,
                                                        int L4, int d4, int G, int per_head) {
@@ -191,7 +203,22 @@ __global__ __launch_bounds__(QO_THREADS) void qo_encode(const float* __restrict_
     const float4 a = make_float4(row[min(src & 0xffu, last)], row[min((src >> 8) & 0xffu, last)],
                                  row[min((src >> 16) & 0xffu, last)], row[min(src >> 24, last)]);
     const float ds = per_head ? descale[h] : ds_t;
-    out[w] = fast_divisor(ds) ? e4m3_word_fast(a, make_divisor(ds)) : e4m3_word(a, ds);
+    float4 qt;                     // the correctly rounded quotients x / ds
+    if (fast_divisor(ds)) {
+      const Divisor dv = make_divisor(ds);
+      qt = make_float4(quotient(a.x, dv), quotient(a.y, dv), quotient(a.z, dv), quotient(a.w, dv));
+      out[w] = e4m3_word_of_quotients(qt);
+    } else {
+      qt = make_float4(a.x / ds, a.y / ds, a.z / ds, a.w / ds);
+      out[w] = e4m3_word(a, ds);
+    }
+    const int js = j - (d - ATTN_OUTLIER_CHANNELS);   // position among the exact channels
+    if (js >= 0) {
+      const int H = L4 / d4;
+      exact[((size_t)r * H + h) * (ATTN_OUTLIER_CHANNELS / 4) + js / 4] =
+          make_uint2(bf16_bits(qt.x) | (bf16_bits(qt.y) << 16),
+                     bf16_bits(qt.z) | (bf16_bits(qt.w) << 16));
+    }
   }
 }
 
@@ -225,8 +252,8 @@ uint32_t* scratch_ptr(int device) {
 }
 
 hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out,
-                                            uint8_t* k_out, float* q_descale,
-                                            float* k_descale, uint8_t* perm,
+                                            uint8_t* k_out, void* q_exact, void* k_exact,
+                                            float* q_descale, float* k_descale, uint8_t* perm,
                                             uint32_t* workspace, int B, int N, int Hq,
                                             int Hkv, int d, int per_head, int q_pow2,
                                             float softmax_scale, hipStream_t stream) {
@@ -251,11 +278,11 @@ hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint
     return (unsigned)std::min<long long>((words + QO_THREADS - 1) / QO_THREADS, 8192);
   };
   hipLaunchKernelGGL(qo_encode, dim3(grid(wq)), dim3(QO_THREADS), 0, stream, q,
-                     (uint32_t*)q_out, (const float*)q_descale, (const uint8_t*)perm, wq, Hq * d4,
-                     d4, Hq / Hkv, per_head);
+                     (uint32_t*)q_out, (uint2*)q_exact, (const float*)q_descale,
+                     (const uint8_t*)perm, wq, Hq * d4, d4, Hq / Hkv, per_head);
   hipLaunchKernelGGL(qo_encode, dim3(grid(wk)), dim3(QO_THREADS), 0, stream, k,
-                     (uint32_t*)k_out, (const float*)k_descale, (const uint8_t*)perm, wk,
-                     Hkv * d4, d4, 1, per_head);
+                     (uint32_t*)k_out, (uint2*)k_exact, (const float*)k_descale,
+                     (const uint8_t*)perm, wk, Hkv * d4, d4, 1, per_head);
   return hipGetLastError();
 }
 

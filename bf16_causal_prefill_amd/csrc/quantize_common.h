@@ -76,6 +76,19 @@ __device__ __forceinline__ float quotient(float a, Divisor d) {
   return copysignf(q, a);
 }
 
+// The code word of four quotients already formed (as e4m3_word_fast below).
+__device__ __forceinline__ uint32_t e4m3_word_of_quotients(float4 q) {
+  if (__builtin_expect(__builtin_isnan((q.x + q.y) + (q.z + q.w)), 0))
+    return e4m3_code(q.x) | (e4m3_code(q.y) << 8) | (e4m3_code(q.z) << 16) |
+           (e4m3_code(q.w) << 24);
+  const float m = 448.f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q.x, -m, m),
+                                          __builtin_amdgcn_fmed3f(q.y, -m, m), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q.z, -m, m),
+                                      __builtin_amdgcn_fmed3f(q.w, -m, m), w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint32_t e4m3_word_fast(float4 a, Divisor d) {
   const float4 q = make_float4(quotient(a.x, d), quotient(a.y, d), quotient(a.z, d),
                                quotient(a.w, d));

@@ -264,9 +264,10 @@ int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale,
  * Permuting the channels of Q and K the same way leaves every score
  * unchanged, so the pair below takes those channels out of the FP8 products:
  * quantize_e4m3_qk_outliers stores each KV head's ATTN_OUTLIER_CHANNELS
- * largest-product channels last, and attn_fwd_causal_fp8_outliers multiplies
- * the last ATTN_OUTLIER_CHANNELS channels of every Q and K row on the BF16
- * matrix instructions (exact products of the e4m3 values, float32 sums).
+ * largest-product channels last and writes them also as bf16 side arrays, and
+ * attn_fwd_causal_fp8_outliers multiplies those last channels of every Q and K
+ * row on the BF16 matrix instructions from the side arrays (exact products,
+ * float32 sums) and the other channels on the FP8 ones from the codes.
  */
 #define ATTN_OUTLIER_CHANNELS 32
 
@@ -283,6 +284,11 @@ int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale,
  *             position j of a row of head h (KV head g = h / (Hq / Hkv) for Q)
  *             holds the code of channel perm[g * d + j]; the codes themselves
  *             are quantize_e4m3's (x / descale rounded to nearest even).
+ *   q_exact, k_exact  DEVICE bf16 side arrays (B, N, Hq, ATTN_OUTLIER_CHANNELS)
+ *             and (B, N, Hkv, ATTN_OUTLIER_CHANNELS), 16-byte aligned: for the
+ *             last ATTN_OUTLIER_CHANNELS stored positions, the bf16 (round to
+ *             nearest even) of the float32 quotient x / descale, i.e. the same
+ *             channels in descale units with 8 instead of 4 significant bits.
  *   q_descale, k_descale  DEVICE float32 outputs, Hq / Hkv values (per_head)
  *             or 1 each: quantize_e4m3's descales; with q_pow2 = 1, Q's is
  *             the one quantize_e4m3_q_pow2 would choose against K's.
@@ -298,7 +304,7 @@ int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale,
  * launch.
  */
 int quantize_e4m3_qk_outliers(const float* q, const float* k,
-                              uint8_t* q_out, uint8_t* k_out,
+                              uint8_t* q_out, uint8_t* k_out, void* q_exact, void* k_exact,
                               float* q_descale, float* k_descale, uint8_t* perm,
                               void* workspace, size_t workspace_bytes,
                               int B, int N, int Hq, int Hkv, int d, int per_head,
@@ -326,23 +332,29 @@ size_t quantize_e4m3_qk_outliers_workspace_bytes(int Hq, int Hkv, int d);
 #define ATTN_NOALLOC_SCRATCH_WORDS 65536
 int quantize_e4m3_qk_outliers_noalloc(const float* q, const float* k,
                                       uint8_t* q_out, uint8_t* k_out,
+                                      void* q_exact, void* k_exact,
                                       float* q_descale, float* k_descale, uint8_t* perm,
                                       int B, int N, int Hq, int Hkv, int d, int per_head,
                                       int q_pow2, float softmax_scale, void* stream);
 
 /*
  * attn_fwd_causal_fp8 and attn_fwd_causal_offset_fp8 with the last
- * ATTN_OUTLIER_CHANNELS channels of every Q and K row multiplied on the BF16
- * matrix instructions (e4m3 values converted exactly; exact products, float32
- * sums) instead of the FP8 ones.  Feed them the codes of
- * quantize_e4m3_qk_outliers (any codes are valid: the result is the same
- * attention, only its accuracy depends on where the large channels are).
+ * ATTN_OUTLIER_CHANNELS channels of every Q and K row taken from bf16 side
+ * arrays and multiplied on the BF16 matrix instructions (exact products,
+ * float32 sums) instead of the FP8 ones: channel c < d_qk - 32 of a Q row has
+ * the value e4m3(q[c]) * q_descale, channel d_qk - 32 + i the value
+ * bf16(q_exact[i]) * q_descale (K alike); the codes of the last 32 channels
+ * are not read.  Feed them the outputs of quantize_e4m3_qk_outliers.
+ *   q_exact (B, N, Hq, 32), k_exact (B, N, Hkv, 32)  DEVICE bf16, 16-byte
+ *             aligned (offset form: Nq rows for q_exact, Nk for k_exact).
  * d_qk must be 128 (else ATTN_E_UNSUPPORTED).  lse may be NULL (then the
  * probabilities take the fast path, as for attn_fwd_causal_fp8).  Everything
- * else as for those entry points.  The extra matrix work is a quarter of the
- * Q.K^T products' FP8 time per exact channel block.
+ * else as for those entry points.  The extra work per key tile is 8 BF16
+ * matrix instructions of 32x32x16 (a quarter of the tile's Q.K^T time) and a
+ * 64-byte side row per key copied with the tile.
  */
 int attn_fwd_causal_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                                 const void* q_exact, const void* k_exact,
                                  const float* q_descale, const float* k_descale,
                                  const float* v_descale, int descale_per_head,
                                  void* o, float* lse,
@@ -350,7 +362,8 @@ int attn_fwd_causal_fp8_outliers(const uint8_t* q, const uint8_t* k, const uint8
                                  float softmax_scale, void* stream);
 
 int attn_fwd_causal_offset_fp8_outliers(const uint8_t* q, const uint8_t* k,
-                                        const uint8_t* v, const float* q_descale,
+                                        const uint8_t* v, const void* q_exact,
+                                        const void* k_exact, const float* q_descale,
                                         const float* k_descale, const float* v_descale,
                                         int descale_per_head, void* o, float* lse,
                                         int B, int Hq, int Hkv, int Nq, int Nk,

@@ -14,7 +14,8 @@ formats    -- exact decoders for bf16 and OCP e4m3fn codes, a round-to-nearest-
               after a block Hadamard rotation (float32 butterflies), and Q
               quantisation with a descale that makes the FP8 softmax constant a
               power of two; joint Q/K quantisation that stores each KV group's
-              largest-product channels last (scores unchanged).
+              largest-product channels last (scores unchanged) with those channels
+              also as bf16 side arrays; a round-to-nearest-even bf16 encoder.
 attention  -- the plain definition of causal softmax attention in float64
               (whole-row softmax, no online/tiled evaluation), over all rows or
               over sampled (b, h, i) rows; the same with Nq queries over Nk keys
@@ -30,7 +31,8 @@ from .formats import (bf16_decode, e4m3_decode, e4m3_encode, quantize_e4m3,
                       absmax_descale, encode_with_descale, E4M3_MAX, hadamard_block,
                       hadamard_unnormalised_fp32, quantize_e4m3_hadamard,
                       quantize_e4m3_q_pow2, pow2_q_descale_one, OUTLIER_CHANNELS,
-                      channel_absmax, outlier_permutation, quantize_e4m3_qk_outliers)
+                      channel_absmax, outlier_permutation, quantize_e4m3_qk_outliers,
+                      bf16_encode, decode_qk_outliers)
 from .attention import (causal_attention, causal_attention_rows, kv_head_of,
                         merge_partials, offset_attention, visible_keys)
 
@@ -38,6 +40,6 @@ __all__ = ["bf16_decode", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "absmax
            "encode_with_descale", "E4M3_MAX", "hadamard_block", "hadamard_unnormalised_fp32",
            "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2", "pow2_q_descale_one",
            "OUTLIER_CHANNELS", "channel_absmax", "outlier_permutation",
-           "quantize_e4m3_qk_outliers",
+           "quantize_e4m3_qk_outliers", "bf16_encode", "decode_qk_outliers",
            "causal_attention", "causal_attention_rows", "kv_head_of", "visible_keys",
            "offset_attention", "merge_partials"]

@@ -242,12 +242,13 @@ def quantize_e4m3_hadamard(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, n
 # ---- Q/K quantisation with the large-product channels moved to the end of the row ----
 # Not on the pages.  The pages name the FP8 error of Q and K as the one that matters
 # (spke.com "ZYFAのFP8アテンションの精度はどのくらいか?"); on the device the FP8 matrix
-# instruction adds up runs of 8 channel products after aligning them to the largest one,
-# so a channel with a large Q or K magnitude swamps the small products that share its
-# run.  Permuting the channels of Q and K the same way leaves every score Q.K unchanged,
-# so the quantiser may store them in any common order: this one moves, per KV head, the
-# n_split channels with the largest product bound to the end of every Q and K row, where
-# the attention that follows can multiply them exactly.  Reading used here:
+# instruction adds up runs of 8 channel products after truncating them to 13 bits below
+# the largest, so a channel with a large Q or K magnitude swamps the small products that
+# share its run.  Permuting the channels of Q and K the same way leaves every score Q.K
+# unchanged, so the quantiser may store them in any common order: this one moves, per KV
+# head, the n_split channels with the largest product bound to the end of every Q and K
+# row, and also writes those channels as bf16 side arrays, which the attention multiplies
+# exactly (in bf16) instead of as e4m3 codes.  Reading used here:
 #   * channel absmax: max |x| over all (b, n) of one head, NaN elements ignored;
 #   * importance of channel c for KV head g: fl32(max over the query heads h of g of
 #     amax_q[h, c]) * amax_k[g, c], in float32, and 0 when either factor is 0;
@@ -255,9 +256,39 @@ def quantize_e4m3_hadamard(x: np.ndarray, per_head: bool) -> tuple[np.ndarray, n
 #     last, in ascending channel order, after the other channels in ascending order;
 #   * codes and descales are those of quantize_e4m3 (or quantize_e4m3_q_pow2 for Q)
 #     of the unpermuted tensor, the codes then permuted: stored position j of a row of
-#     head h holds channel perm[g(h), j].
+#     head h holds channel perm[g(h), j];
+#   * side arrays: for the last n_split stored positions, bf16 (round to nearest even) of
+#     the float32 quotient x / descale, so side value * descale is the channel's value;
+#     the attention reads those channels from the side arrays and not from the codes.
 
 OUTLIER_CHANNELS = 32
+_BF16_NAN = np.uint16(0x7FC0)
+
+
+def bf16_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values -> bf16 bit patterns (uint16), round to nearest even on the value
+    (overflow past the largest bf16 goes to infinity), NaN -> 0x7FC0.
+
+    Written on values: the bf16 neighbours of |x| are the float32 values whose low 16
+    bits are zero; take the nearer, ties to the one whose bf16 mantissa is even."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    u = np.abs(x).view(np.uint32).astype(np.int64)
+    lo = (u >> 16) << 16                                   # truncated neighbour (bits)
+    lo_v = lo.astype(np.uint32).view(np.float32).astype(np.float64)
+    hi = lo + (1 << 16)
+    with np.errstate(over="ignore"):
+        hi_v = np.where(hi >= 0x7F800000, np.inf,
+                        np.minimum(hi, 0x7F7F0000).astype(np.uint32).view(np.float32).astype(np.float64))
+    with np.errstate(invalid="ignore"):      # inf - inf for infinite |x|, overridden below
+        d_lo, d_hi = a - lo_v, hi_v - a
+    even_lo = ((lo >> 16) & 1) == 0
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & ~even_lo)
+    bits = np.where(up, hi >> 16, lo >> 16)
+    bits = np.where(np.isinf(a), 0x7F80, bits)
+    bits = bits | np.where(np.signbit(x), 0x8000, 0)
+    bits = np.where(np.isnan(x), int(_BF16_NAN), bits)
+    return bits.astype(np.uint16)
 
 
 def channel_absmax(x: np.ndarray) -> np.ndarray:
@@ -296,10 +327,12 @@ def quantize_e4m3_qk_outliers(q: np.ndarray, k: np.ndarray, per_head: bool,
                               n_split: int = OUTLIER_CHANNELS,
                               q_pow2_scale: float | None = None):
     """Codes of Q (B, N, Hq, d) and K (B, N, Hkv, d) with each KV group's n_split
-    largest-product channels stored last.  Returns (q_codes, k_codes, q_descale,
-    k_descale, perm): codes uint8 in the permuted channel order, descales as
-    quantize_e4m3 gives them (Q's as quantize_e4m3_q_pow2 with softmax scale
-    q_pow2_scale when that is given), perm (Hkv, d)."""
+    largest-product channels stored last, plus those channels as bf16 side arrays.
+    Returns (q_codes, k_codes, q_exact, k_exact, q_descale, k_descale, perm): codes
+    uint8 in the permuted channel order; q_exact (B, N, Hq, n_split) and k_exact
+    (B, N, Hkv, n_split) bf16 bit patterns (uint16) of x / descale for the last n_split
+    stored channels; descales as quantize_e4m3 gives them (Q's as quantize_e4m3_q_pow2
+    with softmax scale q_pow2_scale when that is given); perm (Hkv, d)."""
     q = np.asarray(q, dtype=np.float32)
     k = np.asarray(k, dtype=np.float32)
     Hq, Hkv = q.shape[2], k.shape[2]
@@ -312,4 +345,28 @@ def quantize_e4m3_qk_outliers(q: np.ndarray, k: np.ndarray, per_head: bool,
     G = Hq // Hkv
     qp = np.stack([qc[:, :, h, perm[h // G]] for h in range(Hq)], axis=2)
     kp = np.stack([kc[:, :, g, perm[g]] for g in range(Hkv)], axis=2)
-    return np.ascontiguousarray(qp), np.ascontiguousarray(kp), qd, kd, perm
+
+    def side(x, ds, heads_perm):
+        out = []
+        for h, pr in enumerate(heads_perm):
+            d_h = np.float32(ds[h] if per_head else ds[0])
+            with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+                quo = (x[:, :, h, pr[-n_split:]] / d_h).astype(np.float32)
+            out.append(bf16_encode(quo))
+        return np.ascontiguousarray(np.stack(out, axis=2))
+    qx = side(q, qd, [perm[h // G] for h in range(Hq)])
+    kx = side(k, kd, [perm[g] for g in range(Hkv)])
+    return (np.ascontiguousarray(qp), np.ascontiguousarray(kp), qx, kx, qd, kd, perm)
+
+
+def decode_qk_outliers(codes: np.ndarray, exact: np.ndarray, descale: np.ndarray,
+                       per_head: bool) -> np.ndarray:
+    """float64 values the exact-channel attention computes with: the e4m3 codes times
+    the descale for the first d - n_split stored channels, the bf16 side values times
+    the descale for the last n_split (whose codes are not read)."""
+    n_split = exact.shape[-1]
+    ds = (np.asarray(descale, np.float64)[None, None, :, None] if per_head
+          else float(np.asarray(descale)[0]))
+    v = e4m3_decode(codes) * ds
+    v[..., -n_split:] = bf16_decode(exact) * ds
+    return v

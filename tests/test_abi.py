@@ -268,29 +268,34 @@ def test_outlier_entry_points_validate():
     vp = ctypes.c_void_p
     f = ctypes.c_float
 
-    def attn(dqk=128, B=1, q=A16):
-        return lib.attn_fwd_causal_fp8_outliers(vp(q), vp(A16), vp(A16), vp(A16), vp(A16),
-                                                vp(A16), 0, vp(A16), vp(None), B, 2, 2, 16,
-                                                dqk, 128, f(0.1), None)
+    def attn(dqk=128, B=1, q=A16, qx=A16, kx=A16):
+        return lib.attn_fwd_causal_fp8_outliers(vp(q), vp(A16), vp(A16), vp(qx), vp(kx),
+                                                vp(A16), vp(A16), vp(A16), 0, vp(A16),
+                                                vp(None), B, 2, 2, 16, dqk, 128, f(0.1), None)
     assert attn(dqk=192) == ba.ATTN_E_UNSUPPORTED
     assert attn(B=0) == ba.ATTN_E_INVAL
+    assert attn(qx=None) == ba.ATTN_E_INVAL
+    assert attn(kx=None) == ba.ATTN_E_INVAL
     assert attn(q=A16 + 4) == ba.ATTN_E_ALIGN
+    assert attn(kx=A16 + 8) == ba.ATTN_E_ALIGN
     assert lib.attn_fwd_causal_offset_fp8_outliers(
-        vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), 0, vp(A16), vp(None), 1, 2, 2,
-        16, 16, -1, 128, 128, f(0.1), None) == ba.ATTN_E_INVAL
+        vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16), 0, vp(A16),
+        vp(None), 1, 2, 2, 16, 16, -1, 128, 128, f(0.1), None) == ba.ATTN_E_INVAL
 
     assert lib.quantize_e4m3_qk_outliers_workspace_bytes(32, 8, 128) == 40 * 128 * 4
     assert lib.quantize_e4m3_qk_outliers_workspace_bytes(0, 8, 128) == 0
 
     def qz(B=1, N=4, Hq=4, Hkv=2, d=128, ph=1, p2=0, s=0.1, ws_bytes=None, q=A16, perm=A16,
-           ws=A16):
+           ws=A16, qx=A16):
         wb = lib.quantize_e4m3_qk_outliers_workspace_bytes(max(Hq, 1), max(Hkv, 1), max(d, 1)) \
             if ws_bytes is None else ws_bytes
-        return lib.quantize_e4m3_qk_outliers(vp(q), vp(A16), vp(A16), vp(A16), vp(A16), vp(A16),
-                                             vp(perm), vp(ws), wb, B, N, Hq, Hkv, d, ph, p2,
-                                             f(s), None)
+        return lib.quantize_e4m3_qk_outliers(vp(q), vp(A16), vp(A16), vp(A16), vp(qx), vp(A16),
+                                             vp(A16), vp(A16), vp(perm), vp(ws), wb, B, N, Hq,
+                                             Hkv, d, ph, p2, f(s), None)
     assert qz(q=None) == ba.ATTN_E_INVAL
     assert qz(ws=None) == ba.ATTN_E_INVAL
+    assert qz(qx=None) == ba.ATTN_E_INVAL
+    assert qz(qx=A16 + 4) == ba.ATTN_E_ALIGN
     assert qz(Hq=3) == ba.ATTN_E_INVAL            # Hq % Hkv
     assert qz(d=28) == ba.ATTN_E_INVAL            # fewer channels than the exact block
     assert qz(d=260) == ba.ATTN_E_INVAL
@@ -311,6 +316,7 @@ def test_binding_rejects_outlier_quantiser_mismatch(no_library):
     q = _t((1, 4, 4, 128), torch.float32)
     k = _t((1, 4, 2, 128), torch.float32)
     a = dict(q=q, k=k, q_out=_t((1, 4, 4, 128), torch.uint8), k_out=_t((1, 4, 2, 128), torch.uint8),
+             q_exact=_t((1, 4, 4, 32), torch.bfloat16), k_exact=_t((1, 4, 2, 32), torch.bfloat16),
              q_descale=_t((4,), torch.float32), k_descale=_t((2,), torch.float32),
              perm=_t((2, 128), torch.uint8), per_head=True)
     with pytest.raises(ValueError, match="perm"):
@@ -319,6 +325,10 @@ def test_binding_rejects_outlier_quantiser_mismatch(no_library):
         ba.quantize_e4m3_qk_outliers(**dict(a, k_descale=_t((1,), torch.float32)))
     with pytest.raises(ValueError, match="k_out: shape"):
         ba.quantize_e4m3_qk_outliers(**dict(a, k_out=_t((1, 4, 4, 128), torch.uint8)))
+    with pytest.raises(ValueError, match="k_exact: shape"):
+        ba.quantize_e4m3_qk_outliers(**dict(a, k_exact=_t((1, 4, 2, 16), torch.bfloat16)))
+    with pytest.raises(ValueError, match="q_exact: dtype"):
+        ba.quantize_e4m3_qk_outliers(**dict(a, q_exact=_t((1, 4, 4, 32), torch.float32)))
     with pytest.raises(ValueError, match="GPU tensor"):
         ba.quantize_e4m3_qk_outliers(**a)
 
@@ -332,8 +342,8 @@ def test_noalloc_quantiser_validates_and_bounds_its_scratch():
 
     def qz(B=1, N=4, Hq=4, Hkv=2, d=128, ph=1, p2=0, s=0.1, q=A16, perm=A16):
         return lib.quantize_e4m3_qk_outliers_noalloc(vp(q), vp(A16), vp(A16), vp(A16), vp(A16),
-                                                     vp(A16), vp(perm), B, N, Hq, Hkv, d, ph,
-                                                     p2, ctypes.c_float(s), None)
+                                                     vp(A16), vp(A16), vp(A16), vp(perm), B, N,
+                                                     Hq, Hkv, d, ph, p2, ctypes.c_float(s), None)
     assert qz(q=None) == ba.ATTN_E_INVAL
     assert qz(Hq=3) == ba.ATTN_E_INVAL
     assert qz(d=28) == ba.ATTN_E_INVAL

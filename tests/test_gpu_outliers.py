@@ -24,22 +24,33 @@ def _bc(ds, per_head):
     return ds[None, None, :, None].astype(np.float64) if per_head else float(ds[0])
 
 
+T = ba.OUTLIER_CHANNELS
+
+
+def _u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
 def outlier_inputs(x, per_head, pow2_scale=None):
     """Q and K through the library's quantize_e4m3_qk_outliers, V through quantize_e4m3,
-    each asserted bit-identical to the oracle; returns device (codes, descale) for q, k,
-    v, the device permutation and the oracle's decoded float64 q, k, v."""
+    each asserted bit-identical to the oracle (codes, bf16 side arrays, descales,
+    permutation); returns device (codes, descale) for q, k, v, the device side arrays
+    (q_exact, k_exact), the device permutation and the oracle's decoded float64 q, k, v
+    (side values for the last 32 channels)."""
     q, k = x["q"], x["k"]
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
-    qc_h, kc_h, qd_h, kd_h, perm_h = oracle.quantize_e4m3_qk_outliers(
+    qc_h, kc_h, qx_h, kx_h, qd_h, kd_h, perm_h = oracle.quantize_e4m3_qk_outliers(
         q, k, per_head, q_pow2_scale=pow2_scale)
     qo = torch.empty(q.shape, device=DEV, dtype=torch.uint8)
     ko = torch.empty(k.shape, device=DEV, dtype=torch.uint8)
+    qx = torch.empty((B, N, Hq, T), device=DEV, dtype=torch.bfloat16)
+    kx = torch.empty((B, N, Hkv, T), device=DEV, dtype=torch.bfloat16)
     qd = torch.empty((Hq if per_head else 1,), device=DEV, dtype=torch.float32)
     kd = torch.empty((Hkv if per_head else 1,), device=DEV, dtype=torch.float32)
     perm = torch.empty((Hkv, d), device=DEV, dtype=torch.uint8)
     ba.quantize_e4m3_qk_outliers(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV), qo, ko,
-                                 qd, kd, perm, per_head, q_pow2=pow2_scale is not None,
+                                 qx, kx, qd, kd, perm, per_head, q_pow2=pow2_scale is not None,
                                  softmax_scale=pow2_scale)
     torch.cuda.synchronize()
     assert np.array_equal(perm.cpu().numpy(), perm_h.astype(np.uint8)), "permutation differs"
@@ -47,20 +58,24 @@ def outlier_inputs(x, per_head, pow2_scale=None):
     assert np.array_equal(kd.cpu().numpy().view(np.uint32), kd_h.view(np.uint32)), "k descale"
     assert np.array_equal(qo.cpu().numpy(), qc_h), "q codes differ from the oracle"
     assert np.array_equal(ko.cpu().numpy(), kc_h), "k codes differ from the oracle"
+    assert np.array_equal(_u16(qx), qx_h), "q side array differs from the oracle"
+    assert np.array_equal(_u16(kx), kx_h), "k side array differs from the oracle"
     vc, vd = gpu_quantize(x["v"], per_head)
     vc_h, vd_h = oracle.quantize_e4m3(x["v"], per_head)
     assert np.array_equal(vc.cpu().numpy(), vc_h)
-    dec = [oracle.e4m3_decode(qc_h) * _bc(qd_h, per_head),
-           oracle.e4m3_decode(kc_h) * _bc(kd_h, per_head),
+    dec = [oracle.decode_qk_outliers(qc_h, qx_h, qd_h, per_head),
+           oracle.decode_qk_outliers(kc_h, kx_h, kd_h, per_head),
            oracle.e4m3_decode(vc_h) * _bc(vd_h, per_head)]
-    return [(qo, qd), (ko, kd), (vc, vd)], perm, dec
+    return [(qo, qd), (ko, kd), (vc, vd)], (qx, kx), perm, dec
 
 
-def run_outliers(dev, per_head, scale, want_lse=True, repeats=1):
+def run_outliers(dev, exact, per_head, scale, want_lse=True, repeats=1):
     (qc, qd), (kc, kd), (vc, vd) = dev
+    qx, kx = exact
     B, N, Hq, _ = qc.shape
     return _repeat(lambda o, lse: ba.attn_fwd_causal_fp8_outliers(
-        qc, kc, vc, qd, kd, vd, o, lse, softmax_scale=scale, descale_per_head=int(per_head)),
+        qc, kc, vc, qx, kx, qd, kd, vd, o, lse, softmax_scale=scale,
+        descale_per_head=int(per_head)),
         B, N, Hq, vc.shape[3], want_lse, repeats,
         "fp8 outliers" + ("" if want_lse else "/no-lse"))[0]
 
@@ -92,7 +107,7 @@ def test_outlier_quantiser_zero_and_tied_channels():
     x = {"q": np.zeros((1, 40, 4, 128), np.float32),
          "k": rng.standard_normal((1, 40, 2, 128)).astype(np.float32),
          "v": rng.standard_normal((1, 40, 2, 128)).astype(np.float32)}
-    dev, perm, _ = outlier_inputs(x, True)
+    dev, _, perm, _ = outlier_inputs(x, True)
     p = perm.cpu().numpy()
     assert np.array_equal(p[0], np.r_[np.arange(32, 128), np.arange(32)])
     assert np.all(dev[0][1].cpu().numpy() == 1.0)
@@ -102,19 +117,25 @@ def test_outlier_quantiser_zero_and_tied_channels():
 
 def test_exact_channels_accumulate_exactly():
     """N = 1 (LSE = the score), scale 1, unit descales.  A 2^14 product with seven 1.0
-    products in its run of 8 channels: in the FP8 channels the ones fall below the
-    run's 13-bit window and are dropped (16384); in the last 32 channels, multiplied
-    on the BF16 pipe, they are kept (16391)."""
+    products in its run of 8 channels: in the FP8 channels (codes) the ones fall below
+    the run's 13-bit window and are dropped (16384); in the last 32 channels, taken from
+    the bf16 side arrays and multiplied on the BF16 pipe, they are kept (16391).  The
+    codes of the last 32 channels are not read: they hold 448s here."""
     q = np.zeros((2, 1, 1, 128), np.uint8)
     k = np.zeros((2, 1, 1, 128), np.uint8)
-    for b, c0 in enumerate((0, 96)):
-        q[b, 0, 0, c0], k[b, 0, 0, c0] = 0x78, 0x68           # 256 * 64
-        q[b, 0, 0, c0 + 1:c0 + 8], k[b, 0, 0, c0 + 1:c0 + 8] = 0x38, 0x38   # 1.0 * 1.0
+    q[..., 96:] = k[..., 96:] = 0x7E                      # ignored codes (448)
+    qx = np.zeros((2, 1, 1, 32), np.uint16)
+    kx = np.zeros((2, 1, 1, 32), np.uint16)
+    q[0, 0, 0, 0], k[0, 0, 0, 0] = 0x78, 0x68              # FP8 run: 256 * 64
+    q[0, 0, 0, 1:8], k[0, 0, 0, 1:8] = 0x38, 0x38          # 1.0 * 1.0
+    qx[1, 0, 0, 0], kx[1, 0, 0, 0] = 0x4380, 0x4280        # exact run: bf16 256 * 64
+    qx[1, 0, 0, 1:8], kx[1, 0, 0, 1:8] = 0x3F80, 0x3F80    # bf16 1.0 * 1.0
     v = np.full((2, 1, 1, 128), 0x38, np.uint8)
     one = torch.ones(1, device=DEV)
     t = lambda a: torch.from_numpy(a).to(DEV)
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
     dev = [(t(q), one), (t(k), one), (t(v), one)]
-    out = run_outliers(dev, False, 1.0)
+    out = run_outliers(dev, (tb(qx), tb(kx)), False, 1.0)
     got = out.lse[:, 0, 0]
     note(f"exact channels: FP8 run {got[0]}, exact run {got[1]} (16384, 16391)")
     assert abs(got[0] - 16384.0) < 0.5 and abs(got[1] - 16391.0) < 0.5
@@ -141,8 +162,8 @@ def test_outlier_attention_parity(case, want_lse, pow2):
     w = SMALL[case]
     note(f"outliers {case} lse={want_lse} pow2={pow2}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N}")
     x = workloads.generate(w)
-    dev, _, (q, k, v) = outlier_inputs(x, w.fp8_per_head, w.softmax_scale if pow2 else None)
-    out = run_outliers(dev, w.fp8_per_head, w.softmax_scale, want_lse=want_lse)
+    dev, ex, _, (q, k, v) = outlier_inputs(x, w.fp8_per_head, w.softmax_scale if pow2 else None)
+    out = run_outliers(dev, ex, w.fp8_per_head, w.softmax_scale, want_lse=want_lse)
     ro, rl = oracle.causal_attention(q, k, v, w.softmax_scale)
     check(f"{case}/outliers", "fp8", out.o, ro, out.lse, rl if want_lse else None,
           fp8_path="exact" if want_lse else "lean",
@@ -150,19 +171,23 @@ def test_outlier_attention_parity(case, want_lse, pow2):
 
 
 def test_outlier_attention_on_plain_codes():
-    """Any codes are valid input: on plain quantize_e4m3 codes (large channels anywhere)
-    the exact-channel kernel still computes the same attention (Gaussian inputs, where
-    no channel stands out)."""
+    """The exact-channel kernel on plain quantize_e4m3 codes with side arrays holding the
+    e4m3 values of their last 32 channels (exact in bf16): the same attention as the
+    plain kernel computes, within the FP8 checks (Gaussian inputs)."""
     w = W["mid_gqa"].with_(N=700, seed=81)
     x = workloads.generate(w)
-    dev, host = [], []
+    dev, host, side = [], [], []
     for n in "qkv":
         c, d = gpu_quantize(x[n], True)
         ch, dh = oracle.quantize_e4m3(x[n], True)
         assert np.array_equal(c.cpu().numpy(), ch)
         dev.append((c, d))
         host.append(oracle.e4m3_decode(ch) * _bc(dh, True))
-    out = run_outliers(dev, True, w.softmax_scale)
+        if n != "v":
+            vals = oracle.e4m3_decode(np.ascontiguousarray(ch[..., -T:])).astype(np.float32)
+            side.append(torch.from_numpy(oracle.bf16_encode(vals).view(np.int16)).to(DEV)
+                        .view(torch.bfloat16))
+    out = run_outliers(dev, tuple(side), True, w.softmax_scale)
     ro, rl = oracle.causal_attention(*host, w.softmax_scale)
     check("plain codes/outliers", "fp8", out.o, ro, out.lse, rl, fp8_path="exact",
           ref_abs_o=abs_v(oracle.causal_attention, *host, w.softmax_scale))
@@ -175,8 +200,8 @@ def test_outlier_attention_full_size_mistral16k(mode):
     w = W["mistral16k"]
     note(f"outliers full mistral16k {mode}")
     x = workloads.generate(w)
-    dev, _, (q, k, v) = outlier_inputs(x, True, w.softmax_scale if mode == "pow2_q" else None)
-    out = run_outliers(dev, True, w.softmax_scale, want_lse=mode != "nolse", repeats=10)
+    dev, ex, _, (q, k, v) = outlier_inputs(x, True, w.softmax_scale if mode == "pow2_q" else None)
+    out = run_outliers(dev, ex, True, w.softmax_scale, want_lse=mode != "nolse", repeats=10)
     rng = np.random.default_rng(7)
     N = w.N
     rows = [(0, h, i) for h in (0, 13, 31) for i in (0, 1, 63, 64, 255, 256, N // 2, N - 1)]
@@ -214,18 +239,20 @@ def test_outlier_offset_attention(case):
         # the joint quantiser wants one N: quantise the padded pair, then slice
         n = max(Nq, Nk)
         pad = lambda a: np.concatenate([a, np.zeros((B, n - a.shape[1]) + a.shape[2:], np.float32)], 1)
-        dev, _, dec = outlier_inputs({"q": pad(x["q"]), "k": pad(x["k"]), "v": pad(x["v"])}, True)
+        dev, ex, _, dec = outlier_inputs({"q": pad(x["q"]), "k": pad(x["k"]), "v": pad(x["v"])},
+                                         True)
         dev = [(dev[0][0][:, :Nq].contiguous(), dev[0][1]), (dev[1][0][:, :Nk].contiguous(), dev[1][1]),
                (dev[2][0][:, :Nk].contiguous(), dev[2][1])]
+        ex = (ex[0][:, :Nq].contiguous(), ex[1][:, :Nk].contiguous())
         dec = [dec[0][:, :Nq], dec[1][:, :Nk], dec[2][:, :Nk]]
     else:
-        dev, _, dec = outlier_inputs(x, True)
+        dev, ex, _, dec = outlier_inputs(x, True)
     (qc, qd), (kc, kd), (vc, vd) = dev
     scale = w.softmax_scale
     o = torch.full((B, Nq, Hq, 128), float("nan"), device=DEV, dtype=torch.bfloat16)
     lse = torch.full((B, Hq, Nq), float("nan"), device=DEV, dtype=torch.float32)
-    ba.attn_fwd_causal_offset_fp8_outliers(qc, kc, vc, qd, kd, vd, o, lse, q_offset=off,
-                                           softmax_scale=scale, descale_per_head=1)
+    ba.attn_fwd_causal_offset_fp8_outliers(qc, kc, vc, ex[0], ex[1], qd, kd, vd, o, lse,
+                                           q_offset=off, softmax_scale=scale, descale_per_head=1)
     torch.cuda.synchronize()
     ro, rl = oracle.offset_attention(*dec, scale, off)
     check(f"offset {case}/outliers", "fp8", o.float().cpu().numpy().astype(np.float64), ro,
@@ -236,6 +263,6 @@ def test_outlier_offset_attention(case):
 def test_outlier_attention_deterministic():
     w = W["mistral16k"].with_(N=4096, seed=83)
     x = workloads.generate(w)
-    dev, _, _ = outlier_inputs(x, True)
-    run_outliers(dev, True, w.softmax_scale, repeats=100)
-    run_outliers(dev, True, w.softmax_scale, want_lse=False, repeats=100)
+    dev, ex, _, _ = outlier_inputs(x, True)
+    run_outliers(dev, ex, True, w.softmax_scale, repeats=100)
+    run_outliers(dev, ex, True, w.softmax_scale, want_lse=False, repeats=100)

@@ -8,6 +8,9 @@ channels last (oracle.quantize_e4m3_qk_outliers), pinned on the CPU:
   importance order, and the rest is a permutation;
 * the codes are quantize_e4m3's (quantize_e4m3_q_pow2's for Q) permuted, with
   bit-identical descales, so every decoded score Q.K is unchanged;
+* the bf16 side arrays of the last 32 stored channels are torch's bf16 cast of the
+  float32 quotient x / descale (the bf16 encoder itself is pinned against that cast),
+  and the decoded values differ from the codes' only by the finer rounding;
 * what the permutation is for, on a model of the FP8 matrix instruction's grouped
   accumulation (the model itself is pinned on the GPU by the accumulation tests in
   test_gpu_parity.py): without the exact channels the LSE of outlier-channel inputs
@@ -93,13 +96,26 @@ def test_brute_force_selection(seed):
         assert perm[g, : d - T].tolist() == sorted(set(range(d)) - set(best))
 
 
+def test_bf16_encoder_matches_torch_cast():
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * s
+                        for s in (1e-38, 1e-20, 1e-3, 1.0, 1e3, 1e30)] +
+                       [np.float32([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 3.39e38,
+                                    -3.39e38, 1.00390625, 1.01171875, 1.0078125])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_encode(x), ref)
+    assert oracle.bf16_encode(np.float32([np.nan]))[0] == 0x7FC0
+
+
 @pytest.mark.parametrize("per_head,pow2", [(True, False), (False, False), (True, True)])
 def test_codes_are_plain_codes_permuted(per_head, pow2):
+    import torch
     w = workloads.CONFIGS["mistral16k"].with_(N=96, Hq=8, Hkv=2, seed=61)
     x = workloads.generate(w)
     scale = w.softmax_scale if pow2 else None
-    qc, kc, qd, kd, perm = oracle.quantize_e4m3_qk_outliers(x["q"], x["k"], per_head,
-                                                            q_pow2_scale=scale)
+    qc, kc, qx, kx, qd, kd, perm = oracle.quantize_e4m3_qk_outliers(x["q"], x["k"], per_head,
+                                                                    q_pow2_scale=scale)
     kc0, kd0 = oracle.quantize_e4m3(x["k"], per_head)
     if pow2:
         qc0, qd0 = oracle.quantize_e4m3_q_pow2(x["q"], per_head, kd0, scale)
@@ -108,21 +124,38 @@ def test_codes_are_plain_codes_permuted(per_head, pow2):
     assert np.array_equal(qd.view(np.uint32), qd0.view(np.uint32))
     assert np.array_equal(kd.view(np.uint32), kd0.view(np.uint32))
     G = w.Hq // w.Hkv
+    T = oracle.OUTLIER_CHANNELS
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     for h in range(w.Hq):
         assert np.array_equal(qc[:, :, h], qc0[:, :, h][..., perm[h // G]])
+        ds = np.float32(qd[h] if per_head else qd[0])
+        assert np.array_equal(qx[:, :, h], bf(x["q"][:, :, h][..., perm[h // G][-T:]] / ds))
     for g in range(w.Hkv):
         assert np.array_equal(kc[:, :, g], kc0[:, :, g][..., perm[g]])
+        ds = np.float32(kd[g] if per_head else kd[0])
+        assert np.array_equal(kx[:, :, g], bf(x["k"][:, :, g][..., perm[g][-T:]] / ds))
     # a common permutation of Q's and K's channels leaves every score unchanged
     bq = lambda c, d_: oracle.e4m3_decode(c) * (d_[None, None, :, None].astype(np.float64)
                                                  if per_head else float(d_[0]))
     s_perm = np.einsum("bihc,bjhc->bhij", bq(qc, qd), np.repeat(bq(kc, kd), G, axis=2))
     s_plain = np.einsum("bihc,bjhc->bhij", bq(qc0, qd0), np.repeat(bq(kc0, kd0), G, axis=2))
     assert np.allclose(s_perm, s_plain, rtol=1e-12, atol=1e-12 * np.abs(s_plain).max())
+    # the side arrays hold the same channels more finely: decoded values within half an
+    # e4m3 step of the codes' values, and within half a bf16 step of x
+    vq = oracle.decode_qk_outliers(qc, qx, qd, per_head)
+    cq = bq(qc, qd)
+    xs = np.stack([x["q"][:, :, h][..., perm[h // G]] for h in range(w.Hq)], axis=2)
+    assert np.array_equal(vq[..., :-T], cq[..., :-T])
+    assert np.all(np.abs(vq[..., -T:] - xs[..., -T:]) <= 2.0 ** -8 * np.abs(xs[..., -T:]) + 1e-30)
+    assert np.all(np.abs(vq[..., -T:] - cq[..., -T:]) <=
+                  2.0 ** -4 * np.abs(xs[..., -T:]) + 2.0 ** -8 * np.abs(xs[..., -T:]) +
+                  2.0 ** -10 * (qd.max() if per_head else qd[0]))
     # the outlier channels of the recipe end up among the stored-last ones
     sq = formats.channel_absmax(x["q"])
     for g in range(w.Hkv):
         top_q = set(np.argsort(-sq[g * G:(g + 1) * G].max(axis=0), kind="stable")[:4].tolist())
-        assert top_q <= set(perm[g, -oracle.OUTLIER_CHANNELS:].tolist())
+        assert top_q <= set(perm[g, -T:].tolist())
 
 
 # ---- the grouped accumulation of the FP8 matrix instruction, modelled ------------------
@@ -166,10 +199,12 @@ def test_grouped_accumulation_model_reproduces_the_measured_cases():
         assert got == want, (a0, b0, a, b, got, want)
 
 
-def _modelled_lse_error(qc, kc, qd, kd, scale, n_exact, rows):
+def _modelled_lse_error(qc, kc, qd, kd, scale, n_exact, rows, qv=None, kv=None):
     """Worst |LSE| change over `rows` when the last n_exact stored channels are
-    multiplied exactly and the rest through the modelled FP8 accumulation."""
-    qv, kv = oracle.e4m3_decode(qc), oracle.e4m3_decode(kc)
+    multiplied exactly and the rest through the modelled FP8 accumulation (qv, kv: the
+    unscaled values, by default the codes' e4m3 values)."""
+    if qv is None:
+        qv, kv = oracle.e4m3_decode(qc), oracle.e4m3_decode(kc)
     qe, ke = _e4m3_exponent(qc), _e4m3_exponent(kc)
     G = qv.shape[2] // kv.shape[2]
     worst = 0.0
@@ -189,11 +224,15 @@ def _modelled_lse_error(qc, kc, qd, kd, scale, n_exact, rows):
 def test_exact_channels_keep_the_lse_inside_the_gate_on_outlier_inputs():
     w = workloads.CONFIGS["mistral16k"].with_(N=512, seed=25)
     x = workloads.generate(w)
-    qc, kc, qd, kd, _ = oracle.quantize_e4m3_qk_outliers(x["q"], x["k"], True)
+    qc, kc, qx, kx, qd, kd, _ = oracle.quantize_e4m3_qk_outliers(x["q"], x["k"], True)
+    one = np.ones_like(qd)
+    qv = oracle.decode_qk_outliers(qc, qx, one, True)      # unscaled (code units)
+    kv = oracle.decode_qk_outliers(kc, kx, np.ones_like(kd), True)
     rng = np.random.default_rng(3)
     rows = [(int(rng.integers(w.Hq)), int(rng.integers(w.N))) for _ in range(800)]
     plain = _modelled_lse_error(qc, kc, qd, kd, w.softmax_scale, 0, rows)
-    split = _modelled_lse_error(qc, kc, qd, kd, w.softmax_scale, oracle.OUTLIER_CHANNELS, rows)
+    split = _modelled_lse_error(qc, kc, qd, kd, w.softmax_scale, oracle.OUTLIER_CHANNELS, rows,
+                                qv=qv, kv=kv)
     print(f"modelled worst LSE error: all channels FP8 {plain:.4f}, "
           f"last {oracle.OUTLIER_CHANNELS} exact {split:.5f}")
     assert plain > 1e-2

@@ -16,16 +16,21 @@ pytestmark = pytest.mark.gpu
 
 def _outputs(x, per_head):
     q, k = x["q"], x["k"]
-    Hq, Hkv, d = q.shape[2], k.shape[2], q.shape[3]
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    T = ba.OUTLIER_CHANNELS
     return (torch.empty(q.shape, device=DEV, dtype=torch.uint8),
             torch.empty(k.shape, device=DEV, dtype=torch.uint8),
+            torch.empty((B, N, Hq, T), device=DEV, dtype=torch.bfloat16),
+            torch.empty((B, N, Hkv, T), device=DEV, dtype=torch.bfloat16),
             torch.empty((Hq if per_head else 1,), device=DEV, dtype=torch.float32),
             torch.empty((Hkv if per_head else 1,), device=DEV, dtype=torch.float32),
             torch.empty((Hkv, d), device=DEV, dtype=torch.uint8))
 
 
 def _host(outs):
-    return [t.cpu().numpy() for t in outs]
+    return [(t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()
+            for t in outs]
 
 
 CALLS = [   # consecutive calls on one device: a larger one, then smaller ones
@@ -48,14 +53,17 @@ def test_noalloc_matches_workspace_entry_point():
         ba.quantize_e4m3_qk_outliers(q, k, *b, per_head, q_pow2=pow2, softmax_scale=scale)
         torch.cuda.synchronize()
         ha, hb = _host(a), _host(b)
-        for name, u, v in zip(("q codes", "k codes", "q descale", "k descale", "perm"), ha, hb):
+        names = ("q codes", "k codes", "q side", "k side", "q descale", "k descale", "perm")
+        for name, u, v in zip(names, ha, hb):
             assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"call {n}: {name}"
-        qc, kc, qd, kd, perm = oracle.quantize_e4m3_qk_outliers(
+        qc, kc, qx, kx, qd, kd, perm = oracle.quantize_e4m3_qk_outliers(
             x["q"], x["k"], per_head, q_pow2_scale=scale if pow2 else None)
         assert np.array_equal(ha[0], qc) and np.array_equal(ha[1], kc), f"call {n}: oracle codes"
-        assert np.array_equal(ha[2].view(np.uint32), qd.view(np.uint32)), f"call {n}"
-        assert np.array_equal(ha[3].view(np.uint32), kd.view(np.uint32)), f"call {n}"
-        assert np.array_equal(ha[4], perm.astype(np.uint8)), f"call {n}: perm"
+        assert np.array_equal(ha[2].view(np.uint16), qx), f"call {n}: q side"
+        assert np.array_equal(ha[3].view(np.uint16), kx), f"call {n}: k side"
+        assert np.array_equal(ha[4].view(np.uint32), qd.view(np.uint32)), f"call {n}"
+        assert np.array_equal(ha[5].view(np.uint32), kd.view(np.uint32)), f"call {n}"
+        assert np.array_equal(ha[6], perm.astype(np.uint8)), f"call {n}: perm"
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():
@@ -65,6 +73,8 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     k = torch.zeros((1, 1, Hkv, 128), device=DEV)
     outs = (torch.empty(q.shape, device=DEV, dtype=torch.uint8),
             torch.empty(k.shape, device=DEV, dtype=torch.uint8),
+            torch.empty((1, 1, Hq, 32), device=DEV, dtype=torch.bfloat16),
+            torch.empty((1, 1, Hkv, 32), device=DEV, dtype=torch.bfloat16),
             torch.empty((Hq,), device=DEV), torch.empty((Hkv,), device=DEV),
             torch.empty((Hkv, 128), device=DEV, dtype=torch.uint8))
     with pytest.raises(ba.AttnError) as e:

@@ -279,6 +279,40 @@ def config_lines(ba, torch, name: str, clock) -> dict:
     return out
 
 
+def other_workload_loop(ba, torch, choice: str):
+    """One call of the attention kernel a profile pass loops on another workload: FP8
+    with the LSE on mla32k (Q for the power-of-two constant), or the exact-channel FP8
+    kernel with the LSE on mistral16k (the joint quantiser's codes and side arrays)."""
+    import workloads
+    dev = "cuda:0"
+    name = "mla32k" if choice == "fp8_mla32k" else "mistral16k"
+    w = workloads.get(name)
+    x = workloads.generate(w)
+    xd = {n: torch.from_numpy(x[n]).to(dev) for n in "qkv"}
+    codes = {n: torch.empty(x[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
+    ds = {n: torch.empty(x[n].shape[2], device=dev) for n in "qkv"}
+    o = torch.empty((w.B, w.N, w.Hq, w.d_v), device=dev, dtype=torch.bfloat16)
+    lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
+    ba.quantize_e4m3(xd["v"], codes["v"], ds["v"], per_head=True)
+    if choice == "fp8_mla32k":
+        ba.quantize_e4m3(xd["k"], codes["k"], ds["k"], per_head=True)
+        ba.quantize_e4m3_q_pow2(xd["q"], codes["q"], ds["q"], ds["k"], w.softmax_scale,
+                                per_head=True)
+        return lambda: ba.attn_fwd_causal_fp8(codes["q"], codes["k"], codes["v"], ds["q"],
+                                              ds["k"], ds["v"], o, lse,
+                                              softmax_scale=w.softmax_scale, descale_per_head=1)
+    T = ba.OUTLIER_CHANNELS
+    qx = torch.empty((w.B, w.N, w.Hq, T), device=dev, dtype=torch.bfloat16)
+    kx = torch.empty((w.B, w.N, w.Hkv, T), device=dev, dtype=torch.bfloat16)
+    perm = torch.empty((w.Hkv, w.d_qk), device=dev, dtype=torch.uint8)
+    ba.quantize_e4m3_qk_outliers(xd["q"], xd["k"], codes["q"], codes["k"], qx, kx, ds["q"],
+                                 ds["k"], perm, True, q_pow2=True, softmax_scale=w.softmax_scale)
+    return lambda: ba.attn_fwd_causal_fp8_outliers(codes["q"], codes["k"], codes["v"], qx, kx,
+                                                   ds["q"], ds["k"], ds["v"], o, lse,
+                                                   softmax_scale=w.softmax_scale,
+                                                   descale_per_head=1)
+
+
 def cpu_baseline(w, x, n_heads: int):
     """The fp64 oracle on query heads 0..n_heads-1 (all N rows) of the workload's
     e4m3-decoded inputs (per-tensor descales from the whole tensors).  Only the
@@ -388,9 +422,13 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--profile-only", action="store_true",
                     help="run the step loop only (for rocprofv3), no JSON line")
-    ap.add_argument("--profile-kernel", choices=("step", "fp8", "bf16"), default="step",
+    ap.add_argument("--profile-kernel",
+                    choices=("step", "fp8", "bf16", "fp8_mla32k", "fp8_outliers_mistral16k"),
+                    default="step",
                     help="with --profile-only: loop the step, the FP8 attention without the "
-                         "LSE, or the BF16 attention with the LSE")
+                         "LSE, the BF16 attention with the LSE, the FP8 attention with the LSE "
+                         "on mla32k, or the exact-channel FP8 attention with the LSE on "
+                         "mistral16k (the outlier path)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -445,6 +483,13 @@ def main() -> int:
         b.record()
         ev_attn.append((a, b))
 
+    if args.profile_only and args.profile_kernel in ("fp8_mla32k", "fp8_outliers_mistral16k"):
+        one = other_workload_loop(ba, torch, args.profile_kernel)
+        for _ in range(args.warmup + args.steps):
+            one()
+        torch.cuda.synchronize()
+        log(f"bench: profile-only {args.profile_kernel} run done")
+        return 0
     if args.profile_only and args.profile_kernel != "step":
         if args.profile_kernel == "fp8":
             quant()

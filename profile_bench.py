@@ -10,8 +10,15 @@ touches the GPU):
   3. --pmc passes of SQ/GRBM counters over the same command (matrix-pipe busy
      cycles, VALU activity, LDS waits and bank conflicts, shader clock);
   4. steps 1 and 3 again for the FP8 kernel without the LSE (Lean P
-     probabilities, row sums on the matrix pipe) and the BF16 kernel with the
-     LSE, each looped alone by `bench.py --profile-only --profile-kernel`.
+     probabilities, row sums on the matrix pipe), the BF16 kernel with the LSE,
+     the FP8 kernel with the LSE on the MLA shape at 32K, and the exact-channel
+     FP8 kernel with the LSE on the Mistral-shaped 16K workload, each looped alone
+     by `bench.py --profile-only --profile-kernel`.
+The shader clock is derived from GRBM_GUI_ACTIVE (summed over the 8 XCDs) divided
+by the kernel's duration from the kernel-trace pass: the dispatch timestamps of
+the counter-collection passes include the profiler's start and stop around each
+dispatch and run about 10% longer, which is why a clock taken over them reads low;
+both figures are written.
 It writes short text summaries plus traffic.json into OUTDIR (which is then
 copied into profiles/).  Raw rocprofv3 output stays in RAWDIR.
 
@@ -31,9 +38,9 @@ sys.path.insert(0, ROOT)
 from bench import kernel_source_sha  # noqa: E402
 
 TAG = "attn_fwd_fp8_d128_lse_gauss32k"
-# the FP8 d128 kernel with LSE, whatever its tile template arguments
-KERNEL = "attn_fwd_kernel<true, 128, *, 1>"
-KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1>")
+# the FP8 d128 kernel with LSE (template: FP8, d_qk, key tile, waves, LSE mode, exact channels)
+KERNEL = "attn_fwd_kernel<true, 128, 128, 8, 1, false>"
+KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, false>")
 # kernel trace: the same step loop bench.py times; counter passes: a shorter loop
 BENCH_KT = ["python", "bench.py", "--profile-only", "--steps", "20", "--warmup", "5"]
 BENCH = ["python", "bench.py", "--profile-only", "--steps", "3", "--warmup", "1"]
@@ -41,10 +48,19 @@ COPY_MIB = 1024
 COPY = ["python", "bench.py", "--copy-only", str(COPY_MIB)]
 # the other two kernels of the metric: (tag, name pattern, profile-kernel choice, title)
 OTHERS = [
-    ("attn_fwd_fp8_d128_gauss32k", re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 0>"), "fp8",
-     "FP8 attention without the LSE (Lean P)"),
-    ("attn_fwd_bf16_d128_lse_gauss32k", re.compile(r"attn_fwd_kernel<false, 128, 64, 8, 1>"),
-     "bf16", "BF16 attention with the LSE"),
+    ("attn_fwd_fp8_d128_gauss32k", re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 0, false>"),
+     "fp8", "FP8 attention without the LSE (Lean P), gauss32k (B=1 Hq=32 Hkv=8 N=32768 d=128)",
+     4.0 * 32 * 32768.0 ** 2 * 128 / 2),
+    ("attn_fwd_bf16_d128_lse_gauss32k", re.compile(r"attn_fwd_kernel<false, 128, 64, 8, 1, false>"),
+     "bf16", "BF16 attention with the LSE, gauss32k (B=1 Hq=32 Hkv=8 N=32768 d=128)",
+     4.0 * 32 * 32768.0 ** 2 * 128 / 2),
+    ("attn_fwd_fp8_d192_lse_mla32k", re.compile(r"attn_fwd_kernel<true, 192, 128, 8, 1, false>"),
+     "fp8_mla32k", "FP8 attention with the LSE, mla32k (B=1 H=16 N=32768 d_qk=192 d_v=128)",
+     2.0 * 16 * 32768.0 ** 2 * 320 / 2),
+    ("attn_fwd_fp8_outliers_d128_lse_mistral16k",
+     re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, true>"), "fp8_outliers_mistral16k",
+     "exact-channel FP8 attention with the LSE, mistral16k (B=1 Hq=32 Hkv=8 N=16384 d=128)",
+     4.0 * 32 * 16384.0 ** 2 * 128 / 2),
 ]
 SQ_PASSES = [
     ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
@@ -90,9 +106,10 @@ def mean_over(vals, key):
     return sum(xs) / len(xs)
 
 
-def sq_summary(prog, kre, raw, name, title, path):
+def sq_summary(prog, kre, raw, name, title, path, trace_ns=None):
     """SQ/GRBM counter passes over `prog` for the kernels matching `kre`, summarised
-    (means per dispatch plus derived ratios) into `path`."""
+    (means per dispatch plus derived ratios) into `path`; trace_ns: the kernel's average
+    duration from its kernel-trace pass (the clock's denominator)."""
     agg, cmdl = {}, []
     for i, p in enumerate(SQ_PASSES):
         d, c = rocprof(["--pmc", *p], prog, raw, f"{name}{i}")
@@ -103,13 +120,17 @@ def sq_summary(prog, kre, raw, name, title, path):
         agg.setdefault("dur_ns", sum(dur.values()) / len(dur))
     xcd, cus, simds = 8, 256, 4
     gui = agg["GRBM_GUI_ACTIVE"] / xcd                     # cycles per XCD
-    sclk = gui / agg["dur_ns"] * 1e3
+    sclk_pmc = gui / agg["dur_ns"] * 1e3
+    sclk = gui / trace_ns * 1e3 if trace_ns else sclk_pmc
     simd_cycles = gui * cus * simds
     lines = [f"# SQ/GRBM counters, {title} (means per dispatch)"]
     lines += [f"# command: {c}" for c in cmdl]
     lines += [f"{k:32s} {v:16.0f}" for k, v in agg.items()]
     lines += ["", "derived:",
-              f"  shader clock             {sclk:8.0f} MHz (GRBM_GUI_ACTIVE / {xcd} XCDs / duration)",
+              f"  shader clock             {sclk:8.0f} MHz (GRBM_GUI_ACTIVE / {xcd} XCDs / "
+              f"kernel-trace duration {trace_ns / 1e3 if trace_ns else float('nan'):.1f} us)",
+              f"  (over the counter pass's own dispatch duration {agg['dur_ns'] / 1e3:.1f} us, "
+              f"which includes the profiler's start/stop: {sclk_pmc:.0f} MHz)",
               f"  MFMA pipe busy           {agg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:8.3f} "
               f"of SIMD cycles",
               f"  VALU co-issued with MFMA {agg['SQ_VALU_MFMA_COEXEC_CYCLES'] / agg['SQ_VALU_MFMA_BUSY_CYCLES']:8.3f} "
@@ -194,10 +215,10 @@ def main() -> int:
 
     # 3. SQ / GRBM counters
     sq_summary(BENCH, KERNEL_RE, raw, "sq", f"{kernel_name}, gauss32k with LSE",
-               os.path.join(out, f"{TAG}_counters.txt"))
+               os.path.join(out, f"{TAG}_counters.txt"), trace_ns=attn_avg_ns)
 
     # 4. the FP8 kernel without the LSE and the BF16 kernel with it
-    for tag, kre, choice, title in OTHERS:
+    for tag, kre, choice, title, kflops in OTHERS:
         prog_kt = BENCH_KT + ["--profile-kernel", choice]
         prog = BENCH + ["--profile-kernel", choice]
         d, cmd = rocprof(["--kernel-trace", "--stats"], prog_kt, raw, f"kt_{choice}")
@@ -207,8 +228,8 @@ def main() -> int:
         for r in rows:
             if kre.search(r["Name"]):
                 name, avg = r["Name"], float(r["AverageNs"])
-        lines = [f"# rocprofv3 kernel statistics: {title}, gauss32k (B=1 Hq=32 Hkv=8 N=32768 "
-                 f"d=128), the kernel looped alone", f"# command: {cmd}", "",
+        lines = [f"# rocprofv3 kernel statistics: {title}, the kernel looped alone",
+                 f"# command: {cmd}", f"# kernel source sha: {kernel_source_sha()}", "",
                  f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
                  f"{'pct':>6s}"]
         for r in rows:
@@ -216,11 +237,11 @@ def main() -> int:
                          f"{float(r['AverageNs'])/1e3:10.1f} {float(r['MinNs'])/1e3:10.1f} "
                          f"{float(r['MaxNs'])/1e3:10.1f} {float(r['Percentage']):6.2f}")
         if avg:
-            lines += ["", f"kernel average {avg/1e3:.1f} us -> {flops / avg / 1e3:.1f} TFLOP/s"]
+            lines += ["", f"kernel average {avg/1e3:.1f} us -> {kflops / avg / 1e3:.1f} TFLOP/s"]
         with open(os.path.join(out, f"{tag}_kernel_stats.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
-        sq_summary(prog, kre, raw, f"sq_{choice}", f"{name}, gauss32k ({title})",
-                   os.path.join(out, f"{tag}_counters.txt"))
+        sq_summary(prog, kre, raw, f"sq_{choice}", f"{name} ({title})",
+                   os.path.join(out, f"{tag}_counters.txt"), trace_ns=avg)
     print("profile summaries written to", out, flush=True)
     return 0
 

@@ -21,10 +21,12 @@ __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal
            "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
            "attn_fwd_causal_offset_fp8_outliers", "OUTLIER_CHANNELS",
            "quantize_e4m3_qk_outliers_noalloc", "NOALLOC_SCRATCH_WORDS",
-           "LIB_PATH",
+           "LIB_PATH", "PHASE_TIMERS_LIB_PATH", "attn_phase_timers_set",
            "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# The measurement build with phase timers (bf16_causal_prefill_amd.build --phase-timers).
+PHASE_TIMERS_LIB_PATH = os.path.join(os.path.dirname(LIB_PATH), "libattn_phase_timers.so")
 EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
                     "attn_merge_partials", "quantize_e4m3", "quantize_e4m3_hadamard",
@@ -103,8 +105,26 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.attn_fwd_causal_offset_fp8_outliers.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
+    if hasattr(L, "attn_phase_timers_set"):          # the measurement build only
+        L.attn_phase_timers_set.argtypes = [vp, ctypes.c_size_t]
+        L.attn_phase_timers_set.restype = i
     _lib = L
     return L
+
+
+def attn_phase_timers_set(buf=None) -> None:
+    """Measurement build (PHASE_TIMERS_LIB_PATH loaded first) only: record the attention
+    kernels' phase timers into buf, a contiguous int64 CUDA tensor (8 waves x 4 words
+    per recorded workgroup, include/attn_phase_timers.h), or stop with None."""
+    L = load_library()
+    if not hasattr(L, "attn_phase_timers_set"):
+        raise RuntimeError("the loaded library is not the phase-timer build")
+    if buf is not None:
+        import torch
+        if not (buf.is_cuda and buf.dtype == torch.int64 and buf.is_contiguous()):
+            raise ValueError("buf must be a contiguous int64 CUDA tensor")
+    nbytes = 0 if buf is None else buf.numel() * 8
+    _check(L.attn_phase_timers_set(_ptr(buf), nbytes), "attn_phase_timers_set")
 
 
 def attn_status_string(status: int) -> str:

@@ -2,6 +2,9 @@
 
 Run as `python -m bf16_causal_prefill_amd.build`.  Each .hip source is compiled
 to an object in parallel, then linked into bf16_causal_prefill_amd/libattn.so.
+`--phase-timers` builds libattn_phase_timers.so instead: the same sources with
+ATTN_PHASE_TIMERS defined (shader-clock reads around the attention kernels' phases,
+include/attn_phase_timers.h), a measurement build that the product never loads.
 """
 from __future__ import annotations
 
@@ -16,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+TIMERS_LIB = os.path.join(PKG, "libattn_phase_timers.so")
 SOURCES = ["api.hip", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "merge.hip", "quantize.hip",
            "outliers.hip"]
 ARCH = "gfx950"
@@ -41,8 +45,8 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, src.replace(".hip", ".o"))
     cmd = [_hipcc(), *HIPFLAGS, *PER_FILE_FLAGS.get(src, []), *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,22 +55,36 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link libattn.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra: list[str] | None = None, verbose: bool = False, lib: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link `lib` (libattn.so); returns the library path."""
+    os.makedirs(build_dir, exist_ok=True)
     extra = list(extra or [])
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_phase_timers(verbose: bool = False) -> str:
+    """The measurement build libattn_phase_timers.so (ATTN_PHASE_TIMERS defined)."""
+    return build(["-DATTN_PHASE_TIMERS"], verbose, TIMERS_LIB,
+                 os.path.join(BUILD, "phase_timers"))
 
 
 if __name__ == "__main__":
-    build(sys.argv[1:], verbose=True)
+    args = sys.argv[1:]
+    if "--phase-timers" in args:
+        args.remove("--phase-timers")
+        if args:
+            raise SystemExit("--phase-timers takes no other arguments")
+        build_phase_timers(verbose=True)
+    else:
+        build(args, verbose=True)

@@ -6,6 +6,9 @@
 #include <stdint.h>
 
 #include "../../include/attn.h"
+#ifdef ATTN_PHASE_TIMERS
+#include "../../include/attn_phase_timers.h"
+#endif
 #include "kernels.h"
 
 namespace {
@@ -50,6 +53,19 @@ int launch_status(hipError_t e) {
   return ATTN_OK;
 }
 
+#ifdef ATTN_PHASE_TIMERS
+// The phase-timer buffer every attention launch of this build records into (set by
+// attn_phase_timers_set; null records nothing).
+unsigned long long* g_timers = nullptr;
+int g_timer_blocks = 0;
+void set_timers(attn::FwdParams& p) {
+  p.timers = g_timers;
+  p.timer_blocks = g_timer_blocks;
+}
+#else
+void set_timers(attn::FwdParams&) {}
+#endif
+
 int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v, float softmax_scale,
              void* stream) {
@@ -62,6 +78,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
+  set_timers(p);
   return launch_status(attn::launch_attn_fwd_bf16(p, d_qk, (hipStream_t)stream));
 }
 
@@ -93,12 +110,25 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   p.k_exact = k_exact;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
+  set_timers(p);
   return launch_status(attn::launch_attn_fwd_fp8(p, d_qk, (hipStream_t)stream));
 }
 
 }  // namespace
 
 extern "C" {
+
+#ifdef ATTN_PHASE_TIMERS
+int attn_phase_timers_set(void* buf, size_t bytes) {
+  if (buf && !aligned(buf, 8)) return ATTN_E_ALIGN;
+  const size_t rec = (size_t)ATTN_PHASE_TIMER_WAVES * ATTN_PHASE_TIMER_WORDS * 8;
+  if (buf && bytes < rec) return ATTN_E_INVAL;
+  const size_t blocks = buf ? bytes / rec : 0;
+  g_timers = (unsigned long long*)buf;
+  g_timer_blocks = blocks > 0x7fffffff ? 0x7fffffff : (int)blocks;
+  return ATTN_OK;
+}
+#endif
 
 int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int Hq, int Hkv, int N, int d_qk, int d_v,

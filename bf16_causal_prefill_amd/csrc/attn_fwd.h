@@ -833,13 +833,32 @@ void attn_fwd_kernel(FwdParams p) {
   // The P2 choice is taken once per workgroup, outside the key loop: each loop copy
   // holds the registers of its own softmax path only (a loop wrapped in a lambda spills,
   // hence the macro).
+#ifdef ATTN_PHASE_TIMERS
+  // Measurement build: shader-clock reads around each phase of the tiles past the
+  // pipeline's fill (t >= 2) and before its drain (t + 2 < n_kt); record layout in
+  // include/attn_phase_timers.h.
+  unsigned tm_mb = 0, tm_vb = 0, tm_t0 = 0, tm_t1 = 0;
+#define ATTN_TM(...) __VA_ARGS__
+#else
+#define ATTN_TM(...)
+#endif
 #define ATTN_KEY_LOOP(P2_TAG)                \
   for (int t = 0; t <= n_kt; ++t) {          \
+    ATTN_TM(const unsigned c0 = (unsigned)__builtin_amdgcn_s_memtime(); \
+            if (t == 2) tm_t0 = c0;          \
+            if (t + 2 == n_kt) tm_t1 = c0;)  \
     mfma_phase(t);                           \
+    ATTN_TM(__builtin_amdgcn_sched_barrier(0); \
+            const unsigned c1 = (unsigned)__builtin_amdgcn_s_memtime(); \
+            if (t >= 2 && t + 2 < n_kt) tm_mb += c1 - c0;) \
     wait_vmcnt<NDMA>();                      \
     phase_barrier();                         \
     if (t < n_kt) {                          \
+      ATTN_TM(const unsigned c2 = (unsigned)__builtin_amdgcn_s_memtime();) \
       valu_phase(t, P2_TAG);                 \
+      ATTN_TM(__builtin_amdgcn_sched_barrier(0); \
+              const unsigned c3 = (unsigned)__builtin_amdgcn_s_memtime(); \
+              if (t >= 2 && t + 2 < n_kt) tm_vb += c3 - c2;) \
       wait_vmcnt<NDMA>();                    \
       phase_barrier();                       \
     }                                        \
@@ -854,9 +873,19 @@ void attn_fwd_kernel(FwdParams p) {
     ATTN_KEY_LOOP(std::false_type{})
   }
 #undef ATTN_KEY_LOOP
+#undef ATTN_TM
   wait_vmcnt<0>();                      // no copy into LDS outlives the loop
   if (!grp_b) phase_barrier();          // equal barrier counts in both groups
   __builtin_amdgcn_s_setprio(0);
+#ifdef ATTN_PHASE_TIMERS
+  if (lane == 0 && p.timers && (int)blockIdx.x < p.timer_blocks) {
+    unsigned long long* rec = p.timers + ((size_t)blockIdx.x * NW + wave) * 4;
+    rec[0] = (unsigned long long)(n_kt > 4 ? n_kt - 4 : 0);
+    rec[1] = tm_mb;
+    rec[2] = tm_vb;
+    rec[3] = n_kt > 4 ? tm_t1 - tm_t0 : 0u;
+  }
+#endif
 
   // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------
   const int qrow = q0w + l32;

@@ -24,6 +24,12 @@ struct FwdParams {
   int split;           // FP8, d_qk 128: the last 32 channels of Q and K on the BF16 pipe,
   const void* q_exact; // from these bf16 side arrays (B, Nq, Hq, 32) and (B, Nk, Hkv, 32)
   const void* k_exact;
+#ifdef ATTN_PHASE_TIMERS
+  // Phase-timer build only (libattn_phase_timers.so): 4 words per (workgroup, wave) of
+  // the first timer_blocks workgroups, see include/attn_phase_timers.h.
+  unsigned long long* timers;
+  int timer_blocks;
+#endif
 };
 
 // Enqueue the causal forward kernel (d_qk 128 or 192; d_v is 128 for both shapes).

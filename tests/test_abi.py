@@ -15,8 +15,11 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 A16 = 0x10000          # an aligned, never-dereferenced stand-in pointer value
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+TIMERS_HEADER = os.path.join(ROOT, "include", "attn_phase_timers.h")
+
+
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -27,6 +30,28 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(ba.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
+    # the phase-timer entry point belongs to the measurement build only
+    for name in _declared_functions(TIMERS_HEADER):
+        assert not hasattr(lib, name), name
+
+
+@pytest.mark.skipif(not os.path.exists(ba.PHASE_TIMERS_LIB_PATH),
+                    reason="libattn_phase_timers.so not built (build.py --phase-timers)")
+def test_phase_timer_build_exports_and_validates():
+    """The measurement build exports include/attn.h's entry points plus
+    include/attn_phase_timers.h's, and its setter checks alignment and size."""
+    lib = ctypes.CDLL(ba.PHASE_TIMERS_LIB_PATH)
+    declared = _declared_functions(TIMERS_HEADER)
+    assert declared == ["attn_phase_timers_set"]
+    for name in _declared_functions() + declared:
+        assert hasattr(lib, name), name
+    fn = lib.attn_phase_timers_set
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    fn.restype = ctypes.c_int
+    assert fn(ctypes.c_void_p(A16 + 4), 4096) == ba.ATTN_E_ALIGN
+    assert fn(ctypes.c_void_p(A16), 8 * 4 * 8 - 8) == ba.ATTN_E_INVAL
+    assert fn(ctypes.c_void_p(A16), 8 * 4 * 8) == ba.ATTN_OK
+    assert fn(None, 0) == ba.ATTN_OK
 
 
 def test_status_strings():

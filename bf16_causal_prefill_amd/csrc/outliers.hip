@@ -53,45 +53,55 @@ __global__ void qo_clear(uint32_t* bits, int n) {
   if (i < n) bits[i] = 0u;
 }
 
-// Per-channel max |x| over the rows r0 .. r1-1 of a (rows, L4) float4 matrix; thread t
-// owns float4 columns t, t + 256, ...  (column c holds channels 4c .. 4c+3 of the flat
-// head-major channel index h*d + ch).  fmaxf ignores NaN elements.
+// Per-channel max |x| of a (rows, L4) float4 matrix (column c holds channels 4c .. 4c+3
+// of the flat head-major channel index h*d + ch).  Workgroup (bx, by) takes the 64 float4
+// columns 64 bx .. (one per lane, so each wave reads 1 KiB of a row) over the rows of band
+// by; its four waves take every fourth row of the band, QO_ROWS_IN_FLIGHT rows at a time,
+// and meet in LDS.  One integer atomicMax per channel and workgroup on the float bits
+// (order-independent): splitting the columns over workgroups keeps the bands, and with
+// them the atomics on each channel, few.  fmaxf ignores NaN elements.
 __global__ __launch_bounds__(QO_THREADS) void qo_channel_absmax(const float* __restrict__ x,
                                                                uint32_t* amax_bits, int rows,
                                                                int L4, int band) {
-  const int r0 = blockIdx.x * band;
+  constexpr int NWAVE = QO_THREADS / 64;
+  __shared__ float4 part[NWAVE][64];
+  const int lane = threadIdx.x & 63, rp = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int r0 = blockIdx.y * band;
   const int r1 = min(rows, r0 + band);
-  for (int c = threadIdx.x; c < L4; c += QO_THREADS) {
-    const float4* col = (const float4*)x + (size_t)r0 * L4 + c;
-    float4 m[QO_ROWS_IN_FLIGHT];
-#pragma unroll
-    for (int u = 0; u < QO_ROWS_IN_FLIGHT; ++u) m[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    int r = r0;
-    for (; r + QO_ROWS_IN_FLIGHT <= r1; r += QO_ROWS_IN_FLIGHT) {
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < L4) {
+    const float4* col = (const float4*)x + c;
+    int r = r0 + rp;
+    for (; r + NWAVE * (QO_ROWS_IN_FLIGHT - 1) < r1; r += NWAVE * QO_ROWS_IN_FLIGHT) {
       float4 a[QO_ROWS_IN_FLIGHT];
 #pragma unroll
-      for (int u = 0; u < QO_ROWS_IN_FLIGHT; ++u) a[u] = load_stream(col + (size_t)u * L4);
-      col += (size_t)QO_ROWS_IN_FLIGHT * L4;
+      for (int u = 0; u < QO_ROWS_IN_FLIGHT; ++u)
+        a[u] = load_stream(col + (size_t)(r + NWAVE * u) * L4);
 #pragma unroll
       for (int u = 0; u < QO_ROWS_IN_FLIGHT; ++u)
-        m[u] = make_float4(fmaxf(m[u].x, fabsf(a[u].x)), fmaxf(m[u].y, fabsf(a[u].y)),
-                           fmaxf(m[u].z, fabsf(a[u].z)), fmaxf(m[u].w, fabsf(a[u].w)));
+        m = make_float4(fmaxf(m.x, fabsf(a[u].x)), fmaxf(m.y, fabsf(a[u].y)),
+                        fmaxf(m.z, fabsf(a[u].z)), fmaxf(m.w, fabsf(a[u].w)));
     }
-    for (; r < r1; ++r) {
-      const float4 a = load_stream(col);
-      col += L4;
-      m[0] = make_float4(fmaxf(m[0].x, fabsf(a.x)), fmaxf(m[0].y, fabsf(a.y)),
-                         fmaxf(m[0].z, fabsf(a.z)), fmaxf(m[0].w, fabsf(a.w)));
+    for (; r < r1; r += NWAVE) {
+      const float4 a = load_stream(col + (size_t)r * L4);
+      m = make_float4(fmaxf(m.x, fabsf(a.x)), fmaxf(m.y, fabsf(a.y)), fmaxf(m.z, fabsf(a.z)),
+                      fmaxf(m.w, fabsf(a.w)));
     }
+  }
+  part[rp][lane] = m;
+  __syncthreads();
+  if (rp == 0 && c < L4) {
 #pragma unroll
-    for (int u = 1; u < QO_ROWS_IN_FLIGHT; ++u)
-      m[0] = make_float4(fmaxf(m[0].x, m[u].x), fmaxf(m[0].y, m[u].y), fmaxf(m[0].z, m[u].z),
-                         fmaxf(m[0].w, m[u].w));
+    for (int w = 1; w < NWAVE; ++w) {
+      const float4 o = part[w][lane];
+      m = make_float4(fmaxf(m.x, o.x), fmaxf(m.y, o.y), fmaxf(m.z, o.z), fmaxf(m.w, o.w));
+    }
     uint32_t* dst = amax_bits + 4 * c;
-    if (m[0].x > 0.f) atomicMax(dst + 0, __float_as_uint(m[0].x));
-    if (m[0].y > 0.f) atomicMax(dst + 1, __float_as_uint(m[0].y));
-    if (m[0].z > 0.f) atomicMax(dst + 2, __float_as_uint(m[0].z));
-    if (m[0].w > 0.f) atomicMax(dst + 3, __float_as_uint(m[0].w));
+    if (m.x > 0.f) atomicMax(dst + 0, __float_as_uint(m.x));
+    if (m.y > 0.f) atomicMax(dst + 1, __float_as_uint(m.y));
+    if (m.z > 0.f) atomicMax(dst + 2, __float_as_uint(m.z));
+    if (m.w > 0.f) atomicMax(dst + 3, __float_as_uint(m.w));
   }
 }
 
@@ -263,12 +273,17 @@ hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint
   uint32_t* amax_k = workspace + (size_t)Hq * d;
   const int nws = (Hq + Hkv) * d;
   hipLaunchKernelGGL(qo_clear, dim3((nws + 255) / 256), dim3(256), 0, stream, workspace, nws);
-  const int band = (rows + QO_ABSMAX_WGS - 1) / QO_ABSMAX_WGS;
-  const int nwg = (rows + band - 1) / band;
-  hipLaunchKernelGGL(qo_channel_absmax, dim3(nwg), dim3(QO_THREADS), 0, stream, q, amax_q, rows,
-                     Hq * d4, band);
-  hipLaunchKernelGGL(qo_channel_absmax, dim3(nwg), dim3(QO_THREADS), 0, stream, k, amax_k, rows,
-                     Hkv * d4, band);
+  // about QO_ABSMAX_WGS workgroups per tensor: 64-column blocks times row bands
+  auto absmax = [&](const float* x, uint32_t* amax, int L4) {
+    const int cb = (L4 + 63) / 64;
+    const int nb0 = std::max(1, std::min(rows, QO_ABSMAX_WGS / cb));
+    const int band = (rows + nb0 - 1) / nb0;
+    const int nb = (rows + band - 1) / band;
+    hipLaunchKernelGGL(qo_channel_absmax, dim3(cb, nb), dim3(QO_THREADS), 0, stream, x, amax,
+                       rows, L4, band);
+  };
+  absmax(q, amax_q, Hq * d4);
+  absmax(k, amax_k, Hkv * d4);
   const float sl = softmax_scale * 1.4426950408889634f;
   hipLaunchKernelGGL(qo_select, dim3(Hkv), dim3(QO_THREADS), 0, stream, (const uint32_t*)amax_q,
                      (const uint32_t*)amax_k, perm, q_descale, k_descale, Hq, Hkv, d, per_head,

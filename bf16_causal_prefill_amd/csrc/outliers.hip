@@ -25,8 +25,8 @@
 //
 // Kernels, in stream order:
 //   1. clear    the per-channel absmax accumulators in the workspace
-//   2. absmax   per-channel max |x| of Q and of K (bands of whole rows per workgroup,
-//               one integer atomicMax per channel and workgroup on the float bits)
+//   2. absmax   per-channel max |x| of Q and of K (64-column blocks times row bands per
+//               workgroup, one integer atomicMax per channel and workgroup on the bits)
 //   3. select   one workgroup per KV head: importance, rank, permutation, descales
 //   4. encode   Q and K rows gathered through the permutation and encoded
 #include <hip/hip_runtime.h>

@@ -592,6 +592,11 @@ def main() -> int:
     if not args.no_cpu:
         log(f"bench: timing the CPU oracle on {args.cpu_heads} heads")
         cpu = cpu_baseline(w, x, args.cpu_heads)
+        # a second sample on the MLA shape (two of its 16 heads), reported beside it
+        import workloads
+        wm = workloads.get("mla32k")
+        log("bench: timing the CPU oracle on 2 heads of mla32k")
+        extra["cpu_baseline_mla32k"] = cpu_baseline(wm, workloads.generate(wm), 2)
 
     # sustained shader clock: sampled from the device during the FP8-with-LSE energy loop
     sclk = (extra.get("energy", {}).get("fp8_attn_lse") or {}).get("sclk_mhz")

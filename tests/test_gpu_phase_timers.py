@@ -1,0 +1,45 @@
+"""The phase-timer measurement build (libattn_phase_timers.so) on the GPU: profile_phases.py
+runs in a child process (the package loads one library per process) on the 4K workload
+and writes a summary whose figures must be complete and consistent for every kernel
+variant and both wave groups: counted tiles present, every phase a positive number of
+cycles, and the period no shorter than the two phases' busy time."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bf16_causal_prefill_amd as ba
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+KERNELS = ["FP8 with LSE, power-of-two Q scale (exact P)", "FP8 with LSE, absmax Q scale (exact P)",
+           "FP8 without LSE (Lean P)", "BF16 with LSE"]
+
+
+@pytest.mark.skipif(not os.path.exists(ba.PHASE_TIMERS_LIB_PATH),
+                    reason="libattn_phase_timers.so not built (build.py --phase-timers)")
+def test_phase_timer_summary(tmp_path):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "profile_phases.py"),
+                        str(tmp_path), "mid_gqa"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=240)
+    print(r.stdout[-3000:])
+    assert r.returncode == 0, r.stderr[-3000:]
+    text = (tmp_path / "phase_timers_mid_gqa.txt").read_text()
+    rows = {}
+    for line in text.splitlines():
+        if line.startswith("#") or not line.strip() or line.startswith("kernel"):
+            continue
+        name, rest = line[:52].strip(), line[52:].split()
+        grp, waves, period, matrix, softmax, wait = rest[0], *map(float, rest[1:])
+        rows[(name, grp)] = (waves, period, matrix, softmax, wait)
+    for k in KERNELS:
+        for grp in "AB":
+            waves, period, matrix, softmax, wait = rows[(k, grp)]
+            assert waves > 0, (k, grp)
+            assert matrix > 0 and softmax > 0, (k, grp, rows[(k, grp)])
+            assert period >= matrix + softmax - 1, (k, grp, rows[(k, grp)])
+            # a key tile takes at least the 16 matrix instructions' 1024 cycles per group
+            assert period >= 1024, (k, grp, rows[(k, grp)])

@@ -2,8 +2,9 @@
 
 One step = the whole FP8 path over one batch of the "gauss32k" workload
 (B=1, Hq=32, Hkv=8, N=32768, d=128, iid N(0,1) inputs already resident in HBM
-as float32): quantize_e4m3 of K and V (per-tensor scales) and quantize_e4m3_q_pow2
-of Q (the per-tensor scale that makes the FP8 softmax constant a power of two), then
+as float32): quantize_e4m3_qkv, which quantises K and V with their absmax scales and Q
+with the per-tensor scale that makes the FP8 softmax constant a power of two (the codes
+of quantize_e4m3 and quantize_e4m3_q_pow2, in four kernels instead of twelve), then
 attn_fwd_causal_fp8 writing O (bf16) and the LSE (fp32).  `value` is the causal
 TFLOP/s of that step, counting only the attention FLOPs 4*B*Hq*N^2*d/2.
 
@@ -76,8 +77,9 @@ def traffic_from_profile(tag: str):
 
 
 def time_events(fn, iters: int, warmup: int = 2) -> float:
-    """Mean duration (ms) of fn() from HIP events on torch's current stream,
-    which is the stream the library launches on."""
+    """Median duration (ms) of fn() from HIP events on torch's current stream,
+    which is the stream the library launches on (the median, so that one delayed
+    launch does not set the figure)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -89,7 +91,8 @@ def time_events(fn, iters: int, warmup: int = 2) -> float:
         fn()
         b.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / iters
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2]
 
 
 def gpu_energy_reader():
@@ -459,13 +462,19 @@ def main() -> int:
     lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
     flops = workloads.causal_flops(w)
 
-    def quant():
+    def quant_separate():
         # K and V with their absmax scales, then Q with the scale that makes the FP8
         # softmax constant a power of two (given K's descales)
         for n in "kv":
             ba.quantize_e4m3(xd[n], codes[n], ds[n], per_head=w.fp8_per_head)
         ba.quantize_e4m3_q_pow2(xd["q"], codes["q"], ds["q"], ds["k"], w.softmax_scale,
                                 per_head=w.fp8_per_head)
+
+    def quant():
+        # the same codes and descales in one call (four kernels instead of twelve)
+        ba.quantize_e4m3_qkv(xd["q"], xd["k"], xd["v"], codes["q"], codes["k"], codes["v"],
+                             ds["q"], ds["k"], ds["v"], per_head=w.fp8_per_head, q_pow2=True,
+                             softmax_scale=w.softmax_scale)
 
     def attn_fp8(with_lse=True):
         ba.attn_fwd_causal_fp8(codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"],
@@ -553,6 +562,8 @@ def main() -> int:
         qbytes = sum(x[n].nbytes * 2 + x[n].size for n in "qkv")   # 2 reads + code write
         extra["quantize_qkv_ms"] = round(t, 4)
         extra["quantize_qkv_GBps"] = round(qbytes / t / 1e6, 1)
+        t = time_events(quant_separate, 10)
+        extra["quantize_qkv_separate_calls_ms"] = round(t, 4)
         xb = {n: xd[n].to(torch.bfloat16) for n in "qkv"}
         for tag, L in (("bf16_attn_lse", lse), ("bf16_attn_nolse", None)):
             t = time_events(lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, L,
@@ -615,8 +626,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
                    "d_qk": w.d_qk, "d_v": w.d_v, "inputs": "iid N(0,1) float32 in HBM",
-                   "step": "quantize_e4m3(k,v) + quantize_e4m3_q_pow2(q), per tensor, "
-                            "+ attn_fwd_causal_fp8 (O + LSE)"},
+                   "step": "quantize_e4m3_qkv (k, v absmax, q power-of-two scale), per "
+                            "tensor, + attn_fwd_causal_fp8 (O + LSE)"},
         "pct_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<fp8, d128> (with LSE)",
                      "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],

@@ -16,7 +16,7 @@ import os
 __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
            "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
            "attn_fwd_causal_offset_fp8_rounded_lse", "attn_merge_partials",
-           "quantize_e4m3", "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2",
+           "quantize_e4m3", "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2", "quantize_e4m3_qkv",
            "attn_status_string", "flash_attn_func", "quantize_e4m3_qk_outliers",
            "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
            "attn_fwd_causal_offset_fp8_outliers", "OUTLIER_CHANNELS",
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_status_string", "quantize_e4m3_qk_outliers",
                     "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
                     "attn_fwd_causal_offset_fp8_outliers",
-                    "quantize_e4m3_qk_outliers_noalloc")
+                    "quantize_e4m3_qk_outliers_noalloc", "quantize_e4m3_qkv")
 
 # Channels per Q/K row that the *_outliers entry points multiply exactly (stored last).
 OUTLIER_CHANNELS = 32
@@ -87,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.quantize_e4m3_q_pow2.argtypes = [vp, vp, vp, i, i, i, i, i, vp, i, f, vp]
     L.quantize_e4m3_q_pow2.restype = i
     L.quantize_e4m3.restype = i
+    L.quantize_e4m3_qkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                    i, f, vp]
+    L.quantize_e4m3_qkv.restype = i
     L.quantize_e4m3_hadamard.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     L.quantize_e4m3_hadamard.restype = i
     L.quantize_e4m3_qk_outliers.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -302,6 +305,38 @@ def quantize_e4m3_q_pow2(x, out, descale, k_descale, softmax_scale: float, per_h
                                              int(bool(per_head)), _ptr(k_descale), Hkv,
                                              float(softmax_scale), _stream(stream))
     _check(st, "quantize_e4m3_q_pow2")
+
+
+def quantize_e4m3_qkv(q, k, v, q_out, k_out, v_out, q_descale, k_descale, v_descale,
+                      per_head: bool, q_pow2: bool = False, softmax_scale=None,
+                      stream=None) -> None:
+    """Q, K and V in one call (four kernels): K and V as quantize_e4m3, Q as
+    quantize_e4m3_q_pow2 against K's descales (q_pow2) or as quantize_e4m3; codes and
+    descales bit-identical to those calls.  q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk),
+    v (B,Nk,Hkv,dv) float32; outputs uint8 of the same shapes and float32 descales of
+    (Hq,) / (Hkv,) / (Hkv,) values (per_head) or (1,)."""
+    B, Nq, Hq, dqk = _rank4(q, "q")
+    _, Nk, Hkv, _ = _rank4(k, "k")
+    dv = _rank4(v, "v")[3]
+    _want(q, "q", "f32", (B, Nq, Hq, dqk))
+    _want(k, "k", "f32", (B, Nk, Hkv, dqk))
+    _want(v, "v", "f32", (B, Nk, Hkv, dv))
+    _want(q_out, "q_out", "e4m3", (B, Nq, Hq, dqk))
+    _want(k_out, "k_out", "e4m3", (B, Nk, Hkv, dqk))
+    _want(v_out, "v_out", "e4m3", (B, Nk, Hkv, dv))
+    _want(q_descale, "q_descale", "f32", (Hq if per_head else 1,))
+    _want(k_descale, "k_descale", "f32", (Hkv if per_head else 1,))
+    _want(v_descale, "v_descale", "f32", (Hkv if per_head else 1,))
+    if q_pow2 and per_head and Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    _on_gpu(q.device, q=q, k=k, v=v, q_out=q_out, k_out=k_out, v_out=v_out,
+            q_descale=q_descale, k_descale=k_descale, v_descale=v_descale)
+    scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
+    st = load_library().quantize_e4m3_qkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(q_descale),
+        _ptr(k_descale), _ptr(v_descale), B, Nq, Nk, Hq, Hkv, dqk, dv, int(bool(per_head)),
+        int(bool(q_pow2)), scale, _stream(stream))
+    _check(st, "quantize_e4m3_qkv")
 
 
 def quantize_e4m3_hadamard(x, out, descale, per_head: bool, stream=None) -> None:

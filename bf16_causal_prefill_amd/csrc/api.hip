@@ -247,6 +247,33 @@ int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale, int B, in
                                                          (hipStream_t)stream));
 }
 
+int quantize_e4m3_qkv(const float* q, const float* k, const float* v, uint8_t* q_out,
+                      uint8_t* k_out, uint8_t* v_out, float* q_descale, float* k_descale,
+                      float* v_descale, int B, int Nq, int Nk, int Hq, int Hkv, int d_qk,
+                      int d_v, int per_head, int q_pow2, float softmax_scale, void* stream) {
+  if (!q || !k || !v || !q_out || !k_out || !v_out || !q_descale || !k_descale || !v_descale)
+    return ATTN_E_INVAL;
+  if (B < 1 || Nq < 1 || Nk < 1 || Hq < 1 || Hkv < 1) return ATTN_E_INVAL;
+  if (d_qk < 4 || (d_qk & 3) != 0 || d_v < 4 || (d_v & 3) != 0) return ATTN_E_INVAL;
+  if (per_head != 0 && per_head != 1) return ATTN_E_INVAL;
+  if (q_pow2 != 0 && q_pow2 != 1) return ATTN_E_INVAL;
+  if (Hq > 65535 || Hkv > 65535) return ATTN_E_INVAL;
+  if (q_pow2 && per_head && Hq % Hkv != 0) return ATTN_E_INVAL;
+  if (q_pow2 && !(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_E_INVAL;
+  if ((long long)B * Nq * Hq * d_qk >= kMaxElems || (long long)B * Nk * Hkv * d_qk >= kMaxElems ||
+      (long long)B * Nk * Hkv * d_v >= kMaxElems)
+    return ATTN_E_INVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_out, 4) ||
+      !aligned(k_out, 4) || !aligned(v_out, 4) || !aligned(q_descale, 4) ||
+      !aligned(k_descale, 4) || !aligned(v_descale, 4))
+    return ATTN_E_ALIGN;
+  const int st = check_device();
+  if (st != ATTN_OK) return st;
+  return launch_status(attn::launch_quantize_e4m3_qkv(
+      q, k, v, q_out, k_out, v_out, q_descale, k_descale, v_descale, B, Nq, Nk, Hq, Hkv, d_qk,
+      d_v, per_head, q_pow2, softmax_scale, (hipStream_t)stream));
+}
+
 int quantize_e4m3_hadamard(const float* x, uint8_t* out, float* descale, int B, int N, int H,
                            int d, int per_head, void* stream) {
   return quantize_impl(x, out, descale, B, N, H, d, per_head, 1, stream);

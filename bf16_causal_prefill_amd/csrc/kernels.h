@@ -51,6 +51,16 @@ hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* desc
                                        const float* k_descale, int Hkv, float softmax_scale,
                                        hipStream_t stream);
 
+// Enqueues the quantisation of Q, K and V in four kernels (clear, absmax, finalize,
+// encode, each over the three tensors); Q as launch_quantize_e4m3_q_pow2 (q_pow2) or
+// launch_quantize_e4m3, K and V as launch_quantize_e4m3.
+hipError_t launch_quantize_e4m3_qkv(const float* q, const float* k, const float* v,
+                                    uint8_t* q_out, uint8_t* k_out, uint8_t* v_out,
+                                    float* q_descale, float* k_descale, float* v_descale,
+                                    int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v,
+                                    int per_head, int q_pow2, float softmax_scale,
+                                    hipStream_t stream);
+
 // Enqueues the joint Q/K quantisation that stores each KV head's largest-product
 // channels last (workspace: (Hq + Hkv) * d uint32 accumulators).
 hipError_t launch_quantize_e4m3_qk_outliers(const float* q, const float* k, uint8_t* q_out,

@@ -112,16 +112,16 @@ __device__ __forceinline__ float absmax4(float4 a) {
 // Bit patterns of non-negative floats order like the values, so maxima are taken as
 // unsigned integers (atomicMax is then exact and order-independent).  With HB4 > 0
 // the values are the Walsh-Hadamard transforms of blocks of 4*HB4 channels.
+// Workgroup `wg` of a pass over one tensor (hmax: the workgroup's LDS maxima).
 template <int HB4>
-__global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict__ x,
-                                                       uint32_t* amax_bits, int rows, int L4,
-                                                       int d4, int H, int per_head, int band) {
+__device__ __forceinline__ void qz_absmax_body(const float* __restrict__ x, uint32_t* amax_bits,
+                                               int rows, int L4, int d4, int H, int per_head,
+                                               int band, int wg, uint32_t* hmax) {
   const int lane = threadIdx.x & 63;
-  __shared__ uint32_t hmax[QZ_LDS_HEADS];
   const int nslots = per_head ? min(H, QZ_LDS_HEADS) : 1;
   for (int i = threadIdx.x; i < nslots; i += QZ_THREADS) hmax[i] = 0u;
   __syncthreads();
-  const int r0 = blockIdx.x * band;
+  const int r0 = wg * band;
   const int r1 = min(rows, r0 + band);
   uint32_t all = 0u;                       // per-tensor mode: this thread's maximum
   for (int c = threadIdx.x; c < L4; c += QZ_THREADS) {
@@ -163,6 +163,14 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict_
     if (hmax[i] != 0u) atomicMax(amax_bits + i, hmax[i]);
 }
 
+template <int HB4>
+__global__ __launch_bounds__(QZ_THREADS) void qz_absmax(const float* __restrict__ x,
+                                                       uint32_t* amax_bits, int rows, int L4,
+                                                       int d4, int H, int per_head, int band) {
+  __shared__ uint32_t hmax[QZ_LDS_HEADS];
+  qz_absmax_body<HB4>(x, amax_bits, rows, L4, d4, H, per_head, band, blockIdx.x, hmax);
+}
+
 // Rows r0 .. r1-1 of float4 column c (FAST: the branch-free word for a divisor in range).
 template <int HB4, bool FAST>
 __device__ __forceinline__ void encode_column(const float4* src, uint32_t* dst, int r0, int r1,
@@ -191,13 +199,13 @@ __device__ __forceinline__ void encode_column(const float4* src, uint32_t* dst, 
 
 // amax_bits holds the absmax bits (ds_final == 0) or the finished descale (ds_final == 1).
 template <int HB4>
-__global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
-                                                       uint32_t* __restrict__ out,
-                                                       const uint32_t* amax_bits, int rows,
-                                                       int L4, int d4, int per_head, int band,
-                                                       int ds_final) {
+__device__ __forceinline__ void qz_encode_body(const float* __restrict__ x,
+                                               uint32_t* __restrict__ out,
+                                               const uint32_t* amax_bits, int rows, int L4,
+                                               int d4, int per_head, int band, int ds_final,
+                                               int wg) {
   const int lane = threadIdx.x & 63;
-  const int r0 = blockIdx.x * band;
+  const int r0 = wg * band;
   const int r1 = min(rows, r0 + band);
   auto ds_of = [&](uint32_t bits) { return ds_final ? __uint_as_float(bits) : descale_of(bits); };
   const float ds_t = per_head ? 0.f : ds_of(amax_bits[0]);
@@ -210,6 +218,15 @@ __global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict_
     else
       encode_column<HB4, false>(src, dst, r0, r1, L4, ds, lane);
   }
+}
+
+template <int HB4>
+__global__ __launch_bounds__(QZ_THREADS) void qz_encode(const float* __restrict__ x,
+                                                       uint32_t* __restrict__ out,
+                                                       const uint32_t* amax_bits, int rows,
+                                                       int L4, int d4, int per_head, int band,
+                                                       int ds_final) {
+  qz_encode_body<HB4>(x, out, amax_bits, rows, L4, d4, per_head, band, ds_final, blockIdx.x);
 }
 
 // descale[i] <- the Q descale above from the absmax it holds (as float bits, which for a
@@ -284,6 +301,111 @@ hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* desc
                      ns, k_descale, group, sl);
   hipLaunchKernelGGL(qz_encode<0>, dim3(nwg), dim3(QZ_THREADS), 0, stream, x, (uint32_t*)out,
                      (const uint32_t*)bits, rows, L4, d4, per_head, band, 1);
+  return hipGetLastError();
+}
+
+// ---- Q, K and V in one call (quantize_e4m3_qkv) ------------------------------------
+// The same passes over the three tensors, one launch each: the grid is the three
+// tensors' workgroups back to back (Q's first, the largest), each workgroup running the
+// pass of the tensor its index falls in.  Codes and descales are those of the separate
+// calls: the same per-element arithmetic, and the finalize below forms the same values.
+struct QzTensor {
+  const float* x;
+  uint32_t* out;
+  uint32_t* bits;      // the tensor's descale array (absmax bits until finalized)
+  int rows, L4, d4, H, band;
+};
+struct QzSet {
+  QzTensor t0, t1, t2;
+  int wg1, wg2;        // first workgroups of tensors 1 and 2
+  int per_head;
+};
+
+// Tensor of workgroup w (field by field, so the set stays in scalar registers).
+__device__ __forceinline__ QzTensor qz_pick(const QzSet& s, int w, int& wg) {
+  const bool in2 = w >= s.wg2, in1 = !in2 && w >= s.wg1;
+  wg = in2 ? w - s.wg2 : in1 ? w - s.wg1 : w;
+  QzTensor t;
+  t.x = in2 ? s.t2.x : in1 ? s.t1.x : s.t0.x;
+  t.out = in2 ? s.t2.out : in1 ? s.t1.out : s.t0.out;
+  t.bits = in2 ? s.t2.bits : in1 ? s.t1.bits : s.t0.bits;
+  t.rows = in2 ? s.t2.rows : in1 ? s.t1.rows : s.t0.rows;
+  t.L4 = in2 ? s.t2.L4 : in1 ? s.t1.L4 : s.t0.L4;
+  t.d4 = in2 ? s.t2.d4 : in1 ? s.t1.d4 : s.t0.d4;
+  t.H = in2 ? s.t2.H : in1 ? s.t1.H : s.t0.H;
+  t.band = in2 ? s.t2.band : in1 ? s.t1.band : s.t0.band;
+  return t;
+}
+
+__global__ void qz_clear3(uint32_t* a, int na, uint32_t* b, int nb, uint32_t* c, int nc) {
+  for (int i = threadIdx.x; i < na + nb + nc; i += blockDim.x) {
+    if (i < na) a[i] = 0u;
+    else if (i < na + nb) b[i - na] = 0u;
+    else c[i - na - nb] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(QZ_THREADS) void qz_absmax3(QzSet s) {
+  __shared__ uint32_t hmax[QZ_LDS_HEADS];
+  int wg;
+  const QzTensor t = qz_pick(s, blockIdx.x, wg);
+  qz_absmax_body<0>(t.x, t.bits, t.rows, t.L4, t.d4, t.H, s.per_head, t.band, wg, hmax);
+}
+
+// One workgroup: Q's descales first, while K's array still holds its absmax bits (the Q
+// power-of-two descale pairs query head i with K's descale descale_of(bits[i / group]),
+// the value K's finalize writes), then K's and V's.
+__global__ void qz_finalize3(float* qd, int nq, float* kd, int nk, float* vd, int nv, int group,
+                             int q_pow2, float sl) {
+  for (int i = threadIdx.x; i < nq; i += blockDim.x)
+    qd[i] = q_pow2 ? pow2_q_descale(qd[i], descale_of(__float_as_uint(kd[i / group])), sl)
+                   : descale_of(__float_as_uint(qd[i]));
+  __syncthreads();
+  for (int i = threadIdx.x; i < nk; i += blockDim.x) kd[i] = descale_of(__float_as_uint(kd[i]));
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) vd[i] = descale_of(__float_as_uint(vd[i]));
+}
+
+__global__ __launch_bounds__(QZ_THREADS) void qz_encode3(QzSet s) {
+  int wg;
+  const QzTensor t = qz_pick(s, blockIdx.x, wg);
+  qz_encode_body<0>(t.x, t.out, t.bits, t.rows, t.L4, t.d4, s.per_head, t.band, 1, wg);
+}
+
+hipError_t launch_quantize_e4m3_qkv(const float* q, const float* k, const float* v,
+                                    uint8_t* q_out, uint8_t* k_out, uint8_t* v_out,
+                                    float* q_descale, float* k_descale, float* v_descale,
+                                    int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v,
+                                    int per_head, int q_pow2, float softmax_scale,
+                                    hipStream_t stream) {
+  auto tensor = [&](const float* x, uint8_t* out, float* ds, int rows, int H, int d, int& nwg) {
+    QzTensor t;
+    t.x = x;
+    t.out = (uint32_t*)out;
+    t.bits = (uint32_t*)ds;
+    t.rows = rows;
+    t.L4 = H * (d / 4);
+    t.d4 = d / 4;
+    t.H = H;
+    t.band = (rows + QZ_TARGET_WGS - 1) / QZ_TARGET_WGS;
+    nwg = (rows + t.band - 1) / t.band;
+    return t;
+  };
+  int nq, nk, nv;
+  QzSet s;
+  s.t0 = tensor(q, q_out, q_descale, B * Nq, Hq, d_qk, nq);
+  s.t1 = tensor(k, k_out, k_descale, B * Nk, Hkv, d_qk, nk);
+  s.t2 = tensor(v, v_out, v_descale, B * Nk, Hkv, d_v, nv);
+  s.wg1 = nq;
+  s.wg2 = nq + nk;
+  s.per_head = per_head;
+  const int sq = per_head ? Hq : 1, skv = per_head ? Hkv : 1;
+  hipLaunchKernelGGL(qz_clear3, dim3(1), dim3(256), 0, stream, s.t0.bits, sq, s.t1.bits, skv,
+                     s.t2.bits, skv);
+  hipLaunchKernelGGL(qz_absmax3, dim3(nq + nk + nv), dim3(QZ_THREADS), 0, stream, s);
+  hipLaunchKernelGGL(qz_finalize3, dim3(1), dim3(256), 0, stream, q_descale, sq, k_descale, skv,
+                     v_descale, skv, per_head ? Hq / Hkv : 1, q_pow2,
+                     softmax_scale * 1.4426950408889634f);
+  hipLaunchKernelGGL(qz_encode3, dim3(nq + nk + nv), dim3(QZ_THREADS), 0, stream, s);
   return hipGetLastError();
 }
 

@@ -226,6 +226,30 @@ int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale,
                          void* stream);
 
 /*
+ * Q, K and V quantised in one call: K and V as quantize_e4m3, Q as
+ * quantize_e4m3_q_pow2 against K's descales (q_pow2 == 1) or as quantize_e4m3
+ * (q_pow2 == 0); codes and descales are bit-identical to those separate calls.
+ * Four kernels are enqueued instead of twelve (each pass runs over the three
+ * tensors in one launch), which saves the short launches' start-up and tail
+ * costs (the per-tensor scale factors: kongchang.com "ZYFA 的性能与精度数据").
+ *   q           DEVICE float32 (B, Nq, Hq, d_qk); k (B, Nk, Hkv, d_qk); v
+ *               (B, Nk, Hkv, d_v); all contiguous and 16-byte aligned.
+ *   q_out, k_out, v_out  DEVICE uint8 codes of the same shapes, 4-byte aligned.
+ *   q_descale, k_descale, v_descale  DEVICE float32: 1 value each (per_head ==
+ *               0), else Hq, Hkv and Hkv values; used as scratch during the
+ *               call.
+ *   softmax_scale  as for quantize_e4m3_q_pow2 (read only when q_pow2 == 1).
+ * d_qk and d_v must be multiples of 4, Hq and Hkv at most 65535, Hq % Hkv == 0
+ * with q_pow2 and per_head, each tensor below 2^31 elements.  Invalid
+ * arguments return ATTN_E_INVAL / ATTN_E_ALIGN before any launch.
+ */
+int quantize_e4m3_qkv(const float* q, const float* k, const float* v,
+                      uint8_t* q_out, uint8_t* k_out, uint8_t* v_out,
+                      float* q_descale, float* k_descale, float* v_descale,
+                      int B, int Nq, int Nk, int Hq, int Hkv, int d_qk, int d_v,
+                      int per_head, int q_pow2, float softmax_scale, void* stream);
+
+/*
  * quantize_e4m3 of the Hadamard-rotated tensor, the FP8 pre-step for Q and K
  * (spke.com "ZYFAのFP8アテンションの精度はどのくらいか?": most of the FP8
  * error comes from quantising Q, K and V, and a Hadamard rotation of Q and K

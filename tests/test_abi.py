@@ -141,6 +141,34 @@ def test_quantize_q_pow2_rejects():
     assert q(x=A16 + 4) == ba.ATTN_E_ALIGN
 
 
+def test_quantize_qkv_rejects():
+    fn = ba.load_library().quantize_e4m3_qkv
+    vp = ctypes.c_void_p
+
+    def q(q=A16, k=A16, v=A16, qo=A16, ko=A16, vo=A16, qd=A16, kd=A16, vd=A16, B=1, Nq=4, Nk=4,
+          Hq=4, Hkv=2, dqk=8, dv=8, ph=1, p2=1, s=0.1):
+        return fn(vp(q), vp(k), vp(v), vp(qo), vp(ko), vp(vo), vp(qd), vp(kd), vp(vd), B, Nq, Nk,
+                  Hq, Hkv, dqk, dv, ph, p2, s, None)
+    for name in ("q", "k", "v", "qo", "ko", "vo", "qd", "kd", "vd"):
+        assert q(**{name: None}) == ba.ATTN_E_INVAL, name
+    assert q(Nk=0) == ba.ATTN_E_INVAL
+    assert q(dqk=6) == ba.ATTN_E_INVAL
+    assert q(dv=2) == ba.ATTN_E_INVAL
+    assert q(Hkv=3) == ba.ATTN_E_INVAL            # Hq % Hkv != 0 with pow2 and per-head
+    assert q(p2=2) == ba.ATTN_E_INVAL
+    assert q(ph=2) == ba.ATTN_E_INVAL
+    assert q(s=0.0) == ba.ATTN_E_INVAL
+    assert q(Hq=70000, Hkv=70000) == ba.ATTN_E_INVAL
+    assert q(B=1, Nq=1 << 20, Hq=32, dqk=128) == ba.ATTN_E_INVAL   # 2^32 elements
+    assert q(v=A16 + 4) == ba.ATTN_E_ALIGN
+    assert q(vo=A16 + 2) == ba.ATTN_E_ALIGN
+    assert q(kd=A16 + 1) == ba.ATTN_E_ALIGN
+    if _no_device():
+        assert q() == ba.ATTN_E_NODEVICE
+        assert q(Hkv=3, p2=0) == ba.ATTN_E_NODEVICE   # no pairing without the pow2 Q scale
+        assert q(s=0.0, p2=0) == ba.ATTN_E_NODEVICE   # the scale is not read then
+
+
 def _no_device():
     import torch
     return torch.cuda.device_count() == 0
@@ -272,6 +300,20 @@ def test_binding_rejects_quantize_mismatch(no_library):
                                 0.1, per_head=True)
     with pytest.raises(ValueError, match="GPU tensor"):
         ba.quantize_e4m3(x, out, _t((3,), torch.float32), True)
+    k = _t((1, 4, 1, 8), torch.float32)
+    v = _t((1, 4, 1, 4), torch.float32)
+    qkv = dict(q=x, k=k, v=v, q_out=out, k_out=_t((1, 4, 1, 8), torch.uint8),
+               v_out=_t((1, 4, 1, 4), torch.uint8), q_descale=_t((3,), torch.float32),
+               k_descale=_t((1,), torch.float32), v_descale=_t((1,), torch.float32),
+               per_head=True)
+    with pytest.raises(ValueError, match="v_out: shape"):
+        ba.quantize_e4m3_qkv(**{**qkv, "v_out": _t((1, 4, 1, 8), torch.uint8)})
+    with pytest.raises(ValueError, match="k_descale: shape"):
+        ba.quantize_e4m3_qkv(**{**qkv, "k_descale": _t((2,), torch.float32)})
+    with pytest.raises(ValueError, match="k: shape"):
+        ba.quantize_e4m3_qkv(**{**qkv, "k": _t((1, 4, 1, 4), torch.float32)})
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.quantize_e4m3_qkv(**qkv, q_pow2=True)
 
 
 def test_binding_rejects_merge_mismatch(no_library):

@@ -120,6 +120,63 @@ def test_quantize_q_pow2_bit_exact(shape, per_head):
     assert np.array_equal(codes.cpu().numpy(), ch)
 
 
+# (B, Nq, Nk, Hq, Hkv, d_qk, d_v): GQA, Nq != Nk, the MLA dims, a ragged row count,
+# more heads than one quantiser workgroup's columns
+QKV_SHAPES = {"gqa": (1, 300, 300, 8, 2, 128, 128), "chunk": (2, 77, 130, 4, 4, 128, 128),
+              "mla": (1, 65, 65, 4, 4, 192, 128), "tiny": (1, 3, 5, 6, 3, 8, 4),
+              "wide": (1, 40, 40, 64, 8, 128, 128)}
+
+
+@pytest.mark.parametrize("q_pow2", [False, True], ids=["absmax_q", "pow2_q"])
+@pytest.mark.parametrize("per_head", [False, True], ids=["per_tensor", "per_head"])
+@pytest.mark.parametrize("shape", list(QKV_SHAPES))
+def test_quantize_qkv_bit_exact(shape, per_head, q_pow2):
+    """quantize_e4m3_qkv: codes and descales bit-identical to the three separate calls
+    and to the oracle's quantisers (Q with the power-of-two rule against the oracle's K
+    descales, or plain absmax), with an all-zero head and NaN elements in Q, an all-zero
+    V head, and very different magnitudes per head."""
+    B, Nq, Nk, Hq, Hkv, dqk, dv = QKV_SHAPES[shape]
+    note(f"case quantize_qkv {shape} per_head={per_head} q_pow2={q_pow2}")
+    rng = np.random.default_rng(Nq * 7 + Hq + per_head + 2 * q_pow2)
+    mag = lambda H: rng.uniform(1e-3, 40, H)[None, None, :, None]
+    q = (rng.standard_normal((B, Nq, Hq, dqk)) * mag(Hq)).astype(np.float32)
+    k = (rng.standard_normal((B, Nk, Hkv, dqk)) * mag(Hkv)).astype(np.float32)
+    v = (rng.standard_normal((B, Nk, Hkv, dv)) * mag(Hkv)).astype(np.float32)
+    q[:, :, Hq - 1, :] = 0.0
+    q[0, 0, 0, :3] = np.nan
+    v[:, :, 0, :] = 0.0
+    scale = 1.0 / np.sqrt(dqk)
+    kc_h, kd_h = oracle.quantize_e4m3(k, per_head)
+    vc_h, vd_h = oracle.quantize_e4m3(v, per_head)
+    if q_pow2:
+        qc_h, qd_h = oracle.quantize_e4m3_q_pow2(q, per_head, kd_h, scale)
+    else:
+        qc_h, qd_h = oracle.quantize_e4m3(q, per_head)
+    dev = {n: torch.from_numpy(a).to(DEV) for n, a in (("q", q), ("k", k), ("v", v))}
+    ns = {"q": Hq if per_head else 1, "k": Hkv if per_head else 1, "v": Hkv if per_head else 1}
+    fused = {n: (torch.empty(dev[n].shape, device=DEV, dtype=torch.uint8),
+                 torch.full((ns[n],), float("nan"), device=DEV)) for n in "qkv"}
+    ba.quantize_e4m3_qkv(dev["q"], dev["k"], dev["v"], fused["q"][0], fused["k"][0],
+                         fused["v"][0], fused["q"][1], fused["k"][1], fused["v"][1], per_head,
+                         q_pow2=q_pow2, softmax_scale=scale)
+    sep = {n: (torch.empty(dev[n].shape, device=DEV, dtype=torch.uint8),
+               torch.empty((ns[n],), device=DEV)) for n in "qkv"}
+    for n in "kv":
+        ba.quantize_e4m3(dev[n], sep[n][0], sep[n][1], per_head)
+    if q_pow2:
+        ba.quantize_e4m3_q_pow2(dev["q"], sep["q"][0], sep["q"][1], sep["k"][1], scale, per_head)
+    else:
+        ba.quantize_e4m3(dev["q"], sep["q"][0], sep["q"][1], per_head)
+    torch.cuda.synchronize()
+    for n, (ch, dh) in (("q", (qc_h, qd_h)), ("k", (kc_h, kd_h)), ("v", (vc_h, vd_h))):
+        fc, fd = (t.cpu().numpy() for t in fused[n])
+        sc, sd = (t.cpu().numpy() for t in sep[n])
+        assert np.array_equal(fd.view(np.uint32), sd.view(np.uint32)), n
+        assert np.array_equal(fc, sc), n
+        assert np.array_equal(fd.view(np.uint32), dh.view(np.uint32)), n
+        assert np.array_equal(fc, ch), n
+
+
 # ---- extreme score patterns ------------------------------------------------------------
 
 def _slope_inputs(N: int, slope_log2: float, seed: int):

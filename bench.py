@@ -18,7 +18,9 @@ kernel runs back to back, and `frac_of_clock_adjusted_peak` the kernel's rate
 against the peak at that clock.  `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workload.  "extra" holds the other precisions and
 shapes of the metric (FP8 with and without the LSE, BF16, the MLA shape at 32K)
-timed the same way, the energy per FLOP of the attention kernels from the
+timed the same way, the step from float32 Q (the attention kernel encoding Q as it
+loads it, after a quantiser pass that writes Q's descales only) beside the step
+above, the energy per FLOP of the attention kernels from the
 device's energy counter, and the entry points past the pages' scope (Hadamard
 pre-step, chunked prefill with a query offset, the merge of partial attentions,
 the flash_attn_func wrapper).
@@ -213,6 +215,36 @@ def timed_with_clock(fn, flops: float, clock=None, seconds: float = 1.0, iters: 
     return ms, flops / ms / 1e9, (round(sum(clk) / len(clk), 1) if clk else None)
 
 
+def float32_q_lines(ba, w, xd, codes, ds, o, lse, flops) -> dict:
+    """The FP8 step with the LSE two ways, timed in alternating rounds: quantize_e4m3_qkv
+    writing Q's codes + attn_fwd_causal_fp8, and quantize_e4m3_qkv with Q's descales only
+    + attn_fwd_causal_fp8_qf32 (the kernel encodes float32 Q as it loads it; O and LSE
+    are byte-identical).  Also the float32-Q attention kernel alone."""
+    ph = int(w.fp8_per_head)
+
+    def quant(q_out):
+        ba.quantize_e4m3_qkv(xd["q"], xd["k"], xd["v"], q_out, codes["k"], codes["v"],
+                             ds["q"], ds["k"], ds["v"], per_head=w.fp8_per_head, q_pow2=True,
+                             softmax_scale=w.softmax_scale)
+
+    attn_codes = lambda: ba.attn_fwd_causal_fp8(
+        codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], o, lse,
+        softmax_scale=w.softmax_scale, descale_per_head=ph)
+    attn_f32 = lambda: ba.attn_fwd_causal_fp8_qf32(
+        xd["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"], o, lse,
+        softmax_scale=w.softmax_scale, descale_per_head=ph)
+    runs = {"codes": (lambda: (quant(codes["q"]), attn_codes())),
+            "f32": (lambda: (quant(None), attn_f32())), "attn_f32": attn_f32}
+    ts = {k: [] for k in runs}
+    for _ in range(3):
+        for k, fn in runs.items():
+            ts[k].append(time_events(fn, 10))
+    med = {k: sorted(v)[len(v) // 2] for k, v in ts.items()}
+    return {"step_q_codes_ms": round(med["codes"], 4),
+            "step_q_float32_ms": round(med["f32"], 4),
+            "fp8_lse_q_float32_tflops": round(flops / med["attn_f32"] / 1e9, 1)}
+
+
 def config_lines(ba, torch, name: str, clock) -> dict:
     """Kernel-only TFLOP/s, % of the dense peak and sustained SCLK of the attention
     kernels on one workload: FP8 with the LSE (Q quantised for the power-of-two softmax
@@ -251,6 +283,7 @@ def config_lines(ba, torch, name: str, clock) -> dict:
     ba.quantize_e4m3_q_pow2(xd["q"], codes["q"], ds["q"], ds["k"], w.softmax_scale,
                             per_head=w.fp8_per_head)
     put("fp8_lse", fp8(lse), "fp8")
+    out.update(float32_q_lines(ba, w, xd, codes, ds, o, lse, flops))
     if w.d_qk == 128:
         # the exact-channel kernel (32 channels on the BF16 pipe), on the joint quantiser's
         # codes with the power-of-two Q scale
@@ -564,6 +597,7 @@ def main() -> int:
         extra["quantize_qkv_GBps"] = round(qbytes / t / 1e6, 1)
         t = time_events(quant_separate, 10)
         extra["quantize_qkv_separate_calls_ms"] = round(t, 4)
+        extra.update(float32_q_lines(ba, w, xd, codes, ds, o, lse, flops))
         xb = {n: xd[n].to(torch.bfloat16) for n in "qkv"}
         for tag, L in (("bf16_attn_lse", lse), ("bf16_attn_nolse", None)):
             t = time_events(lambda: ba.attn_fwd_causal_bf16(xb["q"], xb["k"], xb["v"], o, L,

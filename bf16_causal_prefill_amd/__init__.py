@@ -14,6 +14,7 @@ import math
 import os
 
 __all__ = ["AttnError", "load_library", "attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
+           "attn_fwd_causal_fp8_qf32",
            "attn_fwd_causal_offset_bf16", "attn_fwd_causal_offset_fp8",
            "attn_fwd_causal_offset_fp8_rounded_lse", "attn_merge_partials",
            "quantize_e4m3", "quantize_e4m3_hadamard", "quantize_e4m3_q_pow2", "quantize_e4m3_qkv",
@@ -34,7 +35,8 @@ EXPORTED_SYMBOLS = ("attn_fwd_causal_bf16", "attn_fwd_causal_fp8",
                     "attn_status_string", "quantize_e4m3_qk_outliers",
                     "quantize_e4m3_qk_outliers_workspace_bytes", "attn_fwd_causal_fp8_outliers",
                     "attn_fwd_causal_offset_fp8_outliers",
-                    "quantize_e4m3_qk_outliers_noalloc", "quantize_e4m3_qkv")
+                    "quantize_e4m3_qk_outliers_noalloc", "quantize_e4m3_qkv",
+                    "attn_fwd_causal_fp8_qf32")
 
 # Channels per Q/K row that the *_outliers entry points multiply exactly (stored last).
 OUTLIER_CHANNELS = 32
@@ -72,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.attn_fwd_causal_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp,
                                       i, i, i, i, i, i, f, vp]
     L.attn_fwd_causal_fp8.restype = i
+    L.attn_fwd_causal_fp8_qf32.argtypes = L.attn_fwd_causal_fp8.argtypes
+    L.attn_fwd_causal_fp8_qf32.restype = i
     L.attn_fwd_causal_offset_bf16.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f,
                                               vp]
     L.attn_fwd_causal_offset_bf16.restype = i
@@ -197,12 +201,13 @@ def _rank4(t, name):
     return tuple(int(x) for x in t.shape)
 
 
-def _attn_shapes(q, k, v, kind, same_n):
-    """(B, Hq, Hkv, Nq, Nk, dqk, dv) of q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk), v (B,Nk,Hkv,dv)."""
+def _attn_shapes(q, k, v, kind, same_n, q_kind=None):
+    """(B, Hq, Hkv, Nq, Nk, dqk, dv) of q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk), v (B,Nk,Hkv,dv);
+    q of dtype q_kind when given, else kind."""
     B, Nq, Hq, dqk = _rank4(q, "q")
     _, Nk, Hkv, _ = _rank4(k, "k")
     dv = _rank4(v, "v")[3]
-    _want(q, "q", kind, (B, Nq, Hq, dqk))
+    _want(q, "q", q_kind or kind, (B, Nq, Hq, dqk))
     _want(k, "k", kind, (B, Nk, Hkv, dqk))
     _want(v, "v", kind, (B, Nk, Hkv, dv))
     if same_n and Nk != Nq:
@@ -266,6 +271,24 @@ def attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
     _check(st, "attn_fwd_causal_fp8")
 
 
+def attn_fwd_causal_fp8_qf32(q, k, v, q_descale, k_descale, v_descale, o, lse=None,
+                             softmax_scale=None, descale_per_head=None, stream=None) -> None:
+    """attn_fwd_causal_fp8 with q float32 (B,N,Hq,dqk), encoded by the kernel with
+    q_descale exactly as quantize_e4m3 / quantize_e4m3_q_pow2 encode it (outputs
+    byte-identical to quantising q and calling attn_fwd_causal_fp8); k, v e4m3 codes."""
+    B, Hq, Hkv, N, _, dqk, dv = _attn_shapes(q, k, v, "e4m3", same_n=True, q_kind="f32")
+    _outputs(o, lse, B, N, Hq, dv)
+    descale_per_head = _descales(q_descale, k_descale, v_descale, Hq, Hkv, descale_per_head)
+    _on_gpu(q.device, q=q, k=k, v=v, o=o, lse=lse, q_descale=q_descale, k_descale=k_descale,
+            v_descale=v_descale)
+    scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_causal_fp8_qf32(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        int(descale_per_head), _ptr(o), _ptr(lse), B, Hq, Hkv, N, dqk, dv, scale,
+        _stream(stream))
+    _check(st, "attn_fwd_causal_fp8_qf32")
+
+
 def _quant_args(x, out, descale, per_head, k_descale=None):
     """Checks of the quantisers' arguments (k_descale: quantize_e4m3_q_pow2's);
     returns (B, N, H, d, Hkv)."""
@@ -312,7 +335,8 @@ def quantize_e4m3_qkv(q, k, v, q_out, k_out, v_out, q_descale, k_descale, v_desc
                       stream=None) -> None:
     """Q, K and V in one call (four kernels): K and V as quantize_e4m3, Q as
     quantize_e4m3_q_pow2 against K's descales (q_pow2) or as quantize_e4m3; codes and
-    descales bit-identical to those calls.  q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk),
+    descales bit-identical to those calls (q_out None: Q's descales only, for
+    attn_fwd_causal_fp8_qf32).  q (B,Nq,Hq,dqk), k (B,Nk,Hkv,dqk),
     v (B,Nk,Hkv,dv) float32; outputs uint8 of the same shapes and float32 descales of
     (Hq,) / (Hkv,) / (Hkv,) values (per_head) or (1,)."""
     B, Nq, Hq, dqk = _rank4(q, "q")
@@ -321,7 +345,8 @@ def quantize_e4m3_qkv(q, k, v, q_out, k_out, v_out, q_descale, k_descale, v_desc
     _want(q, "q", "f32", (B, Nq, Hq, dqk))
     _want(k, "k", "f32", (B, Nk, Hkv, dqk))
     _want(v, "v", "f32", (B, Nk, Hkv, dv))
-    _want(q_out, "q_out", "e4m3", (B, Nq, Hq, dqk))
+    if q_out is not None:
+        _want(q_out, "q_out", "e4m3", (B, Nq, Hq, dqk))
     _want(k_out, "k_out", "e4m3", (B, Nk, Hkv, dqk))
     _want(v_out, "v_out", "e4m3", (B, Nk, Hkv, dv))
     _want(q_descale, "q_descale", "f32", (Hq if per_head else 1,))

@@ -86,7 +86,7 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
             const float* k_descale, const float* v_descale, int descale_per_head, void* o,
             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int q_offset, int d_qk, int d_v,
             float softmax_scale, void* stream, int lse_rounded = 0, int split = 0,
-            const void* q_exact = nullptr, const void* k_exact = nullptr) {
+            const void* q_exact = nullptr, const void* k_exact = nullptr, int q_f32 = 0) {
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d_qk, d_v, softmax_scale);
   if (st == ATTN_OK && split && d_qk != 128) st = ATTN_E_UNSUPPORTED;
   if (st == ATTN_OK && split && (!q_exact || !k_exact)) st = ATTN_E_INVAL;
@@ -108,6 +108,7 @@ int fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q
   p.split = split;
   p.q_exact = q_exact;
   p.k_exact = k_exact;
+  p.q_f32 = q_f32;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.q_off = q_offset < Nk ? q_offset : Nk;
   p.scale = softmax_scale;
   set_timers(p);
@@ -143,6 +144,16 @@ int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
                         float softmax_scale, void* stream) {
   return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, descale_per_head, o, lse, B, Hq, Hkv,
                  N, N, 0, d_qk, d_v, softmax_scale, stream);
+}
+
+int attn_fwd_causal_fp8_qf32(const float* q, const uint8_t* k, const uint8_t* v,
+                             const float* q_descale, const float* k_descale,
+                             const float* v_descale, int descale_per_head, void* o, float* lse,
+                             int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                             float softmax_scale, void* stream) {
+  return fwd_fp8((const uint8_t*)q, k, v, q_descale, k_descale, v_descale, descale_per_head, o,
+                 lse, B, Hq, Hkv, N, N, 0, d_qk, d_v, softmax_scale, stream, 0, 0, nullptr,
+                 nullptr, 1);
 }
 
 int attn_fwd_causal_offset_bf16(const void* q, const void* k, const void* v, void* o,
@@ -251,7 +262,7 @@ int quantize_e4m3_qkv(const float* q, const float* k, const float* v, uint8_t* q
                       uint8_t* k_out, uint8_t* v_out, float* q_descale, float* k_descale,
                       float* v_descale, int B, int Nq, int Nk, int Hq, int Hkv, int d_qk,
                       int d_v, int per_head, int q_pow2, float softmax_scale, void* stream) {
-  if (!q || !k || !v || !q_out || !k_out || !v_out || !q_descale || !k_descale || !v_descale)
+  if (!q || !k || !v || !k_out || !v_out || !q_descale || !k_descale || !v_descale)
     return ATTN_E_INVAL;
   if (B < 1 || Nq < 1 || Nk < 1 || Hq < 1 || Hkv < 1) return ATTN_E_INVAL;
   if (d_qk < 4 || (d_qk & 3) != 0 || d_v < 4 || (d_v & 3) != 0) return ATTN_E_INVAL;
@@ -263,7 +274,7 @@ int quantize_e4m3_qkv(const float* q, const float* k, const float* v, uint8_t* q
   if ((long long)B * Nq * Hq * d_qk >= kMaxElems || (long long)B * Nk * Hkv * d_qk >= kMaxElems ||
       (long long)B * Nk * Hkv * d_v >= kMaxElems)
     return ATTN_E_INVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_out, 4) ||
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (q_out && !aligned(q_out, 4)) ||
       !aligned(k_out, 4) || !aligned(v_out, 4) || !aligned(q_descale, 4) ||
       !aligned(k_descale, 4) || !aligned(v_descale, 4))
     return ATTN_E_ALIGN;

@@ -58,6 +58,7 @@
 
 #include "attn_common.h"
 #include "kernels.h"
+#include "quantize_common.h"
 
 namespace attn {
 
@@ -83,6 +84,12 @@ struct Cfg {
   static constexpr int KX_BYTES = BN * KX_ROW;
   static constexpr int KXDMA = KX_BYTES / (1024 * NW);
   static constexpr int LDS_SPLIT = LDS + NKS * KX_BYTES;
+  // float32 Q (FP8): each wave turns the codes of one 64-channel k-step of its 32 rows
+  // from row order into the MFMA operand order through a private LDS block past the
+  // stages, rows padded from 64 to 80 bytes (16-byte reads of 8 consecutive rows hit
+  // 8 different 4-bank groups)
+  static constexpr int QX_ROW = 80;
+  static constexpr int LDS_QF32 = LDS + NW * 32 * QX_ROW;
   static constexpr int KS = FP8 ? DQK / 64 : DQK / 16;  // MFMA k-steps of Q K^T
   static constexpr int MT = BN / 32;                 // 32-key M-tiles of S^T
   static constexpr int NB = BN / 64;                 // 64-key blocks
@@ -92,10 +99,11 @@ struct Cfg {
   static_assert(LDS <= 160 * 1024, "LDS budget of a workgroup");
   static_assert(!FP8 || DQK != 128 || (LDS_SPLIT <= 160 * 1024 && KXDMA == 1),
                 "LDS budget and copy split of the exact-channel kernel");
+  static_assert(!FP8 || LDS_QF32 <= 160 * 1024, "LDS budget of the float32-Q kernel");
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
 };
 
-template <bool FP8, int DQK, int BN, int NW, int LSE, bool SPLIT>
+template <bool FP8, int DQK, int BN, int NW, int LSE, bool SPLIT, bool QF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
@@ -111,6 +119,8 @@ void attn_fwd_kernel(FwdParams p) {
   // KV head's largest-product channels there.  The BF16 products are exact and their
   // float32 sums as accurate as float32.
   static_assert(!SPLIT || (FP8 && DQK == 128 && LSE != 2), "exact channels: FP8, d_qk 128");
+  // QF32 (FP8): Q is float32 and encoded on load (see the prologue)
+  static_assert(!QF32 || (FP8 && !SPLIT), "float32 Q: the FP8 kernels without exact channels");
   constexpr int NSPC = 32;                               // exact channels (stored last)
   constexpr bool WANT_LSE = LSE != 0;
   constexpr bool EXACT = FP8 && LSE == 1;
@@ -137,8 +147,9 @@ void attn_fwd_kernel(FwdParams p) {
   // Softmax constant in log2 units per raw score unit (descales folded in for FP8).
   float c = p.scale * LOG2E;
   float vds = 1.f;
+  float dq = 1.f;   // FP8: Q's descale (float32 Q is encoded with it in the prologue)
   if (FP8) {
-    const float dq = p.qds[p.per_head ? h : 0];
+    dq = p.qds[p.per_head ? h : 0];
     const float dk = p.kds[p.per_head ? hkv : 0];
     vds = p.vds[p.per_head ? hkv : 0];
     c *= dq * dk;
@@ -167,7 +178,21 @@ void attn_fwd_kernel(FwdParams p) {
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
   QFrag qf[C::KS];
   bf16x8 qsp[SPLIT ? NSPC / 16 : 1];   // exact channels of Q^T, one per BF16 k-step
-  {
+  // QF32: float32 Q read in row order, whole rows per load: q32[8ks + i] holds channels
+  // 64ks + 4(lane & 15) .. +3 of the wave's row 4i + lane / 16 (16 lanes cover the 256
+  // contiguous bytes of one k-step of a row), encoded into qf in the prologue
+  float4 q32[QF32 ? 8 * C::KS : 1];
+  if constexpr (QF32) {
+    const size_t qstride = (size_t)p.Hq * DQK * 4;
+    const char* qbase = (const char*)p.q + ((size_t)b * Nq * p.Hq + h) * DQK * 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(q0w + 4 * i + (lane >> 4), Nq - 1);
+      const float4* rp = (const float4*)(qbase + (size_t)row * qstride) + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) q32[8 * ks + i] = rp[16 * ks];
+    }
+  } else {
     const size_t qstride = (size_t)p.Hq * DQK * C::EB;
     const char* qbase = (const char*)p.q + ((size_t)b * Nq * p.Hq + h) * DQK * C::EB;
     const int qrow = min(q0w + l32, Nq - 1);
@@ -823,6 +848,38 @@ void attn_fwd_kernel(FwdParams p) {
   // would sink the P V MFMAs into a branch that followed them).
   zero_p();                             // the first matrix phase has no P yet
   copy_tile(0);
+  if constexpr (QF32) {
+    // The codes quantize_e4m3 / quantize_e4m3_q_pow2 write with this descale (round to
+    // nearest even of x / descale, saturating at +-448, NaN to 0x7F; the same encoder),
+    // formed while the first tile is being copied, then moved to the operand order one
+    // k-step at a time through the wave's LDS block: code word 4i + lane / 16, lane & 15
+    // of the row-order block, read back as 32 bytes of row l32 at byte 32g.  The block
+    // is this wave's alone and a wave's LDS accesses execute in issue order, so fences
+    // at wavefront scope (ordering for the compiler, no wait) are all it needs.
+    const float dsq = dq;
+    uint32_t qw[8 * C::KS];
+    if (fast_divisor(dsq)) {
+      const Divisor dv = make_divisor(dsq);
+#pragma unroll
+      for (int e = 0; e < 8 * C::KS; ++e) qw[e] = e4m3_word_fast(q32[e], dv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8 * C::KS; ++e) qw[e] = e4m3_word(q32[e], dsq);
+    }
+    char* const qx = lds + C::LDS + wave * 32 * C::QX_ROW;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint32_t*)(qx + (4 * i + (lane >> 4)) * C::QX_ROW + 4 * (lane & 15)) = qw[8 * ks + i];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint4* src = (const uint4*)(qx + l32 * C::QX_ROW + 32 * g);
+      const uint4 lo = src[0], hi = src[1];
+      qf[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+  }
   // The Q fragments and tile 0 have landed (loads complete in issue order); the
   // compiler also learns here that nothing it issued is outstanding.
   wait_vmcnt<0>();
@@ -918,21 +975,28 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false>
-                     : attn_fwd_kernel<FP8, DQK, BN, NW, 1, false>;
+  auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, false>
+                     : attn_fwd_kernel<FP8, DQK, BN, NW, 1, false, false>;
   if constexpr (FP8) {
-    if (p.lse && p.lse_rounded) kern = attn_fwd_kernel<FP8, DQK, BN, NW, 2, false>;
+    if (p.lse && p.lse_rounded) kern = attn_fwd_kernel<FP8, DQK, BN, NW, 2, false, false>;
+    if (p.q_f32) {
+      if (p.lse_rounded || p.split) return hipErrorInvalidValue;
+      kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, true>
+                    : attn_fwd_kernel<FP8, DQK, BN, NW, 1, false, true>;
+    }
+  } else {
+    if (p.q_f32) return hipErrorInvalidValue;
   }
   if constexpr (FP8 && DQK == 128) {
     if (p.split) {
       if (p.lse_rounded) return hipErrorInvalidValue;
-      kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, true>
-                    : attn_fwd_kernel<FP8, DQK, BN, NW, 1, true>;
+      kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, true, false>
+                    : attn_fwd_kernel<FP8, DQK, BN, NW, 1, true, false>;
     }
   } else {
     if (p.split) return hipErrorInvalidValue;
   }
-  const int lds = p.split ? C::LDS_SPLIT : C::LDS;
+  const int lds = p.split ? C::LDS_SPLIT : p.q_f32 ? C::LDS_QF32 : C::LDS;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;

@@ -24,6 +24,7 @@ struct FwdParams {
   int split;           // FP8, d_qk 128: the last 32 channels of Q and K on the BF16 pipe,
   const void* q_exact; // from these bf16 side arrays (B, Nq, Hq, 32) and (B, Nk, Hkv, 32)
   const void* k_exact;
+  int q_f32;           // FP8: q is float32, encoded on load with q's descales
 #ifdef ATTN_PHASE_TIMERS
   // Phase-timer build only (libattn_phase_timers.so): 4 words per (workgroup, wave) of
   // the first timer_blocks workgroups, see include/attn_phase_timers.h.
@@ -53,7 +54,8 @@ hipError_t launch_quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* desc
 
 // Enqueues the quantisation of Q, K and V in four kernels (clear, absmax, finalize,
 // encode, each over the three tensors); Q as launch_quantize_e4m3_q_pow2 (q_pow2) or
-// launch_quantize_e4m3, K and V as launch_quantize_e4m3.
+// launch_quantize_e4m3, K and V as launch_quantize_e4m3.  q_out null: Q's descales
+// only.
 hipError_t launch_quantize_e4m3_qkv(const float* q, const float* k, const float* v,
                                     uint8_t* q_out, uint8_t* k_out, uint8_t* v_out,
                                     float* q_descale, float* k_descale, float* v_descale,

@@ -405,7 +405,18 @@ hipError_t launch_quantize_e4m3_qkv(const float* q, const float* k, const float*
   hipLaunchKernelGGL(qz_finalize3, dim3(1), dim3(256), 0, stream, q_descale, sq, k_descale, skv,
                      v_descale, skv, per_head ? Hq / Hkv : 1, q_pow2,
                      softmax_scale * 1.4426950408889634f);
-  hipLaunchKernelGGL(qz_encode3, dim3(nq + nk + nv), dim3(QZ_THREADS), 0, stream, s);
+  if (q_out) {
+    hipLaunchKernelGGL(qz_encode3, dim3(nq + nk + nv), dim3(QZ_THREADS), 0, stream, s);
+  } else {
+    // Q's descales only (for the attention entry points that take float32 Q): the
+    // encode pass covers K and V
+    QzSet e = s;
+    e.t0 = s.t1;
+    e.t1 = s.t2;
+    e.wg1 = nk;
+    e.wg2 = nk + nv;
+    hipLaunchKernelGGL(qz_encode3, dim3(nk + nv), dim3(QZ_THREADS), 0, stream, e);
+  }
   return hipGetLastError();
 }
 

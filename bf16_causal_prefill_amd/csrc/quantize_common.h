@@ -76,9 +76,15 @@ __device__ __forceinline__ float quotient(float a, Divisor d) {
   return copysignf(q, a);
 }
 
+// NaN test on the bit pattern, which holds also where the compiler is told that no
+// NaNs occur (the FP8 attention kernels, which encode float32 Q with these helpers).
+__device__ __forceinline__ bool nan_bits(float x) {
+  return (__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u;
+}
+
 // The code word of four quotients already formed (as e4m3_word_fast below).
 __device__ __forceinline__ uint32_t e4m3_word_of_quotients(float4 q) {
-  if (__builtin_expect(__builtin_isnan((q.x + q.y) + (q.z + q.w)), 0))
+  if (__builtin_expect(nan_bits((q.x + q.y) + (q.z + q.w)), 0))
     return e4m3_code(q.x) | (e4m3_code(q.y) << 8) | (e4m3_code(q.z) << 16) |
            (e4m3_code(q.w) << 24);
   const float m = 448.f;
@@ -92,7 +98,7 @@ __device__ __forceinline__ uint32_t e4m3_word_of_quotients(float4 q) {
 __device__ __forceinline__ uint32_t e4m3_word_fast(float4 a, Divisor d) {
   const float4 q = make_float4(quotient(a.x, d), quotient(a.y, d), quotient(a.z, d),
                                quotient(a.w, d));
-  if (__builtin_expect(__builtin_isnan((q.x + q.y) + (q.z + q.w)), 0))
+  if (__builtin_expect(nan_bits((q.x + q.y) + (q.z + q.w)), 0))
     return e4m3_code(q.x) | (e4m3_code(q.y) << 8) | (e4m3_code(q.z) << 16) |
            (e4m3_code(q.w) << 24);
   const float m = 448.f;

@@ -109,6 +109,24 @@ int attn_fwd_causal_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v,
                         float softmax_scale, void* stream);
 
 /*
+ * attn_fwd_causal_fp8 on float32 Q: q is DEVICE float32 (B, N, Hq, d_qk),
+ * 16-byte aligned, and q_descale its descales (from quantize_e4m3,
+ * quantize_e4m3_q_pow2, or quantize_e4m3_qkv with q_out == NULL).  The kernel
+ * encodes each Q row as it loads it, with the quantisers' encoder (round to
+ * nearest even of x / descale, saturating at +-448, NaN to 0x7F), so O and the
+ * LSE are byte-identical to quantising Q and calling attn_fwd_causal_fp8; the
+ * separate pass that writes Q's codes (a read of the float32 tensor and a write
+ * of a quarter of its size) is not needed.  Other arguments and the results as
+ * for attn_fwd_causal_fp8 (d_qk 128 or 192).
+ */
+int attn_fwd_causal_fp8_qf32(const float* q, const uint8_t* k, const uint8_t* v,
+                             const float* q_descale, const float* k_descale,
+                             const float* v_descale, int descale_per_head,
+                             void* o, float* lse,
+                             int B, int Hq, int Hkv, int N, int d_qk, int d_v,
+                             float softmax_scale, void* stream);
+
+/*
  * Causal attention of Nq queries over Nk keys with a query offset: key j is
  * visible to query i iff j <= i + q_offset.  This is the same computation with
  * the causal diagonal shifted, for query chunks that follow a KV prefix
@@ -235,6 +253,8 @@ int quantize_e4m3_q_pow2(const float* x, uint8_t* out, float* descale,
  *   q           DEVICE float32 (B, Nq, Hq, d_qk); k (B, Nk, Hkv, d_qk); v
  *               (B, Nk, Hkv, d_v); all contiguous and 16-byte aligned.
  *   q_out, k_out, v_out  DEVICE uint8 codes of the same shapes, 4-byte aligned.
+ *               q_out may be NULL: then only Q's descales are computed, for
+ *               attn_fwd_causal_fp8_qf32, which encodes float32 Q itself.
  *   q_descale, k_descale, v_descale  DEVICE float32: 1 value each (per_head ==
  *               0), else Hq, Hkv and Hkv values; used as scratch during the
  *               call.

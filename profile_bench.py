@@ -38,9 +38,10 @@ sys.path.insert(0, ROOT)
 from bench import kernel_source_sha  # noqa: E402
 
 TAG = "attn_fwd_fp8_d128_lse_gauss32k"
-# the FP8 d128 kernel with LSE (template: FP8, d_qk, key tile, waves, LSE mode, exact channels)
-KERNEL = "attn_fwd_kernel<true, 128, 128, 8, 1, false>"
-KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, false>")
+# the FP8 d128 kernel with LSE (template: FP8, d_qk, key tile, waves, LSE mode, exact
+# channels, float32 Q)
+KERNEL = "attn_fwd_kernel<true, 128, 128, 8, 1, false, false>"
+KERNEL_RE = re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, false, false>")
 # kernel trace: the same step loop bench.py times; counter passes: a shorter loop
 BENCH_KT = ["python", "bench.py", "--profile-only", "--steps", "20", "--warmup", "5"]
 BENCH = ["python", "bench.py", "--profile-only", "--steps", "3", "--warmup", "1"]
@@ -48,17 +49,17 @@ COPY_MIB = 1024
 COPY = ["python", "bench.py", "--copy-only", str(COPY_MIB)]
 # the other two kernels of the metric: (tag, name pattern, profile-kernel choice, title)
 OTHERS = [
-    ("attn_fwd_fp8_d128_gauss32k", re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 0, false>"),
+    ("attn_fwd_fp8_d128_gauss32k", re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 0, false, false>"),
      "fp8", "FP8 attention without the LSE (Lean P), gauss32k (B=1 Hq=32 Hkv=8 N=32768 d=128)",
      4.0 * 32 * 32768.0 ** 2 * 128 / 2),
-    ("attn_fwd_bf16_d128_lse_gauss32k", re.compile(r"attn_fwd_kernel<false, 128, 64, 8, 1, false>"),
+    ("attn_fwd_bf16_d128_lse_gauss32k", re.compile(r"attn_fwd_kernel<false, 128, 64, 8, 1, false, false>"),
      "bf16", "BF16 attention with the LSE, gauss32k (B=1 Hq=32 Hkv=8 N=32768 d=128)",
      4.0 * 32 * 32768.0 ** 2 * 128 / 2),
-    ("attn_fwd_fp8_d192_lse_mla32k", re.compile(r"attn_fwd_kernel<true, 192, 128, 8, 1, false>"),
+    ("attn_fwd_fp8_d192_lse_mla32k", re.compile(r"attn_fwd_kernel<true, 192, 128, 8, 1, false, false>"),
      "fp8_mla32k", "FP8 attention with the LSE, mla32k (B=1 H=16 N=32768 d_qk=192 d_v=128)",
      2.0 * 16 * 32768.0 ** 2 * 320 / 2),
     ("attn_fwd_fp8_outliers_d128_lse_mistral16k",
-     re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, true>"), "fp8_outliers_mistral16k",
+     re.compile(r"attn_fwd_kernel<true, 128, 128, 8, 1, true, false>"), "fp8_outliers_mistral16k",
      "exact-channel FP8 attention with the LSE, mistral16k (B=1 Hq=32 Hkv=8 N=16384 d=128)",
      4.0 * 32 * 16384.0 ** 2 * 128 / 2),
 ]

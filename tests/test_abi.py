@@ -149,7 +149,7 @@ def test_quantize_qkv_rejects():
           Hq=4, Hkv=2, dqk=8, dv=8, ph=1, p2=1, s=0.1):
         return fn(vp(q), vp(k), vp(v), vp(qo), vp(ko), vp(vo), vp(qd), vp(kd), vp(vd), B, Nq, Nk,
                   Hq, Hkv, dqk, dv, ph, p2, s, None)
-    for name in ("q", "k", "v", "qo", "ko", "vo", "qd", "kd", "vd"):
+    for name in ("q", "k", "v", "ko", "vo", "qd", "kd", "vd"):
         assert q(**{name: None}) == ba.ATTN_E_INVAL, name
     assert q(Nk=0) == ba.ATTN_E_INVAL
     assert q(dqk=6) == ba.ATTN_E_INVAL
@@ -167,6 +167,33 @@ def test_quantize_qkv_rejects():
         assert q() == ba.ATTN_E_NODEVICE
         assert q(Hkv=3, p2=0) == ba.ATTN_E_NODEVICE   # no pairing without the pow2 Q scale
         assert q(s=0.0, p2=0) == ba.ATTN_E_NODEVICE   # the scale is not read then
+        assert q(qo=None) == ba.ATTN_E_NODEVICE       # Q's descales only
+        assert q(qo=None, q=A16 + 4) == ba.ATTN_E_ALIGN
+
+
+def test_fp8_qf32_entry_validates():
+    """The float32-Q entry point shares the FP8 checks (shape, scale, alignment,
+    descales) and takes the same argument list."""
+    lib = ba.load_library()
+    vp = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=A16, k=A16, v=A16, qd=A16, kd=A16, vd=A16, ph=0, o=A16, lse=None, B=1, Hq=2,
+                 Hkv=2, N=16, dqk=128, dv=128, scale=0.1)
+        a.update(kw)
+        return lib.attn_fwd_causal_fp8_qf32(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["qd"]),
+                                            vp(a["kd"]), vp(a["vd"]), a["ph"], vp(a["o"]),
+                                            vp(a["lse"]), a["B"], a["Hq"], a["Hkv"], a["N"],
+                                            a["dqk"], a["dv"], a["scale"], None)
+    assert call(q=None) == ba.ATTN_E_INVAL
+    assert call(qd=None) == ba.ATTN_E_INVAL
+    assert call(Hq=3) == ba.ATTN_E_INVAL
+    assert call(scale=-1.0) == ba.ATTN_E_INVAL
+    assert call(dqk=64) == ba.ATTN_E_UNSUPPORTED
+    assert call(q=A16 + 8) == ba.ATTN_E_ALIGN
+    assert call(ph=2) == ba.ATTN_E_INVAL
+    if _no_device():
+        assert call() == ba.ATTN_E_NODEVICE
 
 
 def _no_device():
@@ -314,6 +341,16 @@ def test_binding_rejects_quantize_mismatch(no_library):
         ba.quantize_e4m3_qkv(**{**qkv, "k": _t((1, 4, 1, 4), torch.float32)})
     with pytest.raises(ValueError, match="GPU tensor"):
         ba.quantize_e4m3_qkv(**qkv, q_pow2=True)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.quantize_e4m3_qkv(**{**qkv, "q_out": None})     # Q's descales only: accepted
+    q8, k8 = _t((1, 8, 4, 128), torch.uint8), _t((1, 8, 2, 128), torch.uint8)
+    d4, d2 = _t((4,), torch.float32), _t((2,), torch.float32)
+    o = _t((1, 8, 4, 128), torch.bfloat16)
+    with pytest.raises(ValueError, match="q: dtype"):
+        ba.attn_fwd_causal_fp8_qf32(q8, k8, k8.clone(), d4, d2, d2.clone(), o)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ba.attn_fwd_causal_fp8_qf32(_t((1, 8, 4, 128), torch.float32), k8, k8.clone(), d4, d2,
+                                    d2.clone(), o)
 
 
 def test_binding_rejects_merge_mismatch(no_library):

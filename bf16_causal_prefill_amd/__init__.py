@@ -121,7 +121,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def attn_phase_timers_set(buf=None) -> None:
     """Measurement build (PHASE_TIMERS_LIB_PATH loaded first) only: record the attention
-    kernels' phase timers into buf, a contiguous int64 CUDA tensor (8 waves x 4 words
+    kernels' phase timers into buf, a contiguous int64 CUDA tensor (8 waves x 10 words
     per recorded workgroup, include/attn_phase_timers.h), or stop with None."""
     L = load_library()
     if not hasattr(L, "attn_phase_timers_set"):

@@ -59,6 +59,14 @@
 #include "attn_common.h"
 #include "kernels.h"
 #include "quantize_common.h"
+#ifdef ATTN_PHASE_TIMERS
+#include "../../include/attn_phase_timers.h"
+// s_getreg operands (id | offset << 6 | (bits - 1) << 11): the wave's hardware ids
+// (wave, SIMD, CU in bits 8-11, shader array, shader engine in bits 13-15, ...) and the
+// index of its compute die
+#define HWREG_HW_ID (4 | (31 << 11))
+#define HWREG_XCC_ID (20 | (15 << 11))
+#endif
 
 namespace attn {
 
@@ -131,6 +139,9 @@ void attn_fwd_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int g = lane >> 5;
+#ifdef ATTN_PHASE_TIMERS
+  const unsigned long long rt_entry = __builtin_amdgcn_s_memrealtime();
+#endif
 
   int b, h, qt;
   map_block(blockIdx.x, p, b, h, qt);
@@ -886,6 +897,9 @@ void attn_fwd_kernel(FwdParams p) {
   copy_tile(1);
   phase_barrier();
   if (grp_b) phase_barrier();           // group B runs half a phase behind group A
+#ifdef ATTN_PHASE_TIMERS
+  const unsigned long long rt_loop0 = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // The P2 choice is taken once per workgroup, outside the key loop: each loop copy
   // holds the registers of its own softmax path only (a loop wrapped in a lambda spills,
@@ -935,13 +949,7 @@ void attn_fwd_kernel(FwdParams p) {
   if (!grp_b) phase_barrier();          // equal barrier counts in both groups
   __builtin_amdgcn_s_setprio(0);
 #ifdef ATTN_PHASE_TIMERS
-  if (lane == 0 && p.timers && (int)blockIdx.x < p.timer_blocks) {
-    unsigned long long* rec = p.timers + ((size_t)blockIdx.x * NW + wave) * 4;
-    rec[0] = (unsigned long long)(n_kt > 4 ? n_kt - 4 : 0);
-    rec[1] = tm_mb;
-    rec[2] = tm_vb;
-    rec[3] = n_kt > 4 ? tm_t1 - tm_t0 : 0u;
-  }
+  const unsigned long long rt_loop1 = __builtin_amdgcn_s_memrealtime();
 #endif
 
   // ---- epilogue: normalise, write O (bf16) and LSE ---------------------------------
@@ -951,8 +959,20 @@ void attn_fwd_kernel(FwdParams p) {
   if (EXACT) l = lx_run + xor32(lx_run);
   const float lsum = l;
   const float inv = (FP8 ? vds : 1.f) / l;
-  if (qrow < Nq) {
-    __bf16* orow = (__bf16*)p.o + ((size_t)((size_t)b * Nq + qrow) * p.Hq + h) * DV;
+  // O leaves through LDS so that each store instruction writes whole rows: the wave's
+  // 32 rows go to a private block (rows padded from 256 to 272 bytes, so the 8-byte
+  // writes of one column of the accumulators spread over the banks), then each lane
+  // stores 16 contiguous bytes, 16 lanes per row, 4 rows per instruction (full cache
+  // lines, a quarter of the write requests of storing from the accumulator layout,
+  // where every instruction touches 32 rows).  The stages are free once every wave's
+  // copies have landed (the barrier below; each wave waited for its own above), and a
+  // wave's LDS accesses execute in issue order, so its own block needs only a
+  // wavefront fence between the writes and the reads.
+  phase_barrier();
+  {
+    constexpr int OROW = DV * 2 + 16;
+    static_assert(8 * 32 * OROW <= C::LDS, "O staging fits in the stages");
+    char* const ost = lds + wave * 32 * OROW;
 #pragma unroll
     for (int md = 0; md < DV / 32; ++md)
 #pragma unroll
@@ -960,12 +980,44 @@ void attn_fwd_kernel(FwdParams p) {
         bf16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[md][4 * r + e] * inv);
-        *(bf16x4*)(orow + 32 * md + 8 * r + 4 * g) = ov;
+        *(bf16x4*)(ost + l32 * OROW + 2 * (32 * md + 8 * r + 4 * g)) = ov;
       }
-    if (WANT_LSE && g == 0)
-      p.lse[((size_t)b * p.Hq + h) * Nq + qrow] =
-          ((EXACT && P2 ? r_run : m_run * c) + __builtin_amdgcn_logf(lsum)) * LN2;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    constexpr int CPR = DV * 2 / 16;          // 16-byte chunks per O row
+    constexpr int RPI = 64 / CPR;             // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = RPI * i + lane / CPR;
+      const uint4 v = *(const uint4*)(ost + rr * OROW + 16 * (lane % CPR));
+      if (q0w + rr < Nq)
+        *(uint4*)((char*)p.o + ((size_t)((size_t)b * Nq + q0w + rr) * p.Hq + h) * DV * 2 +
+                  16 * (lane % CPR)) = v;
+    }
   }
+  if (WANT_LSE && g == 0 && qrow < Nq)
+    p.lse[((size_t)b * p.Hq + h) * Nq + qrow] =
+        ((EXACT && P2 ? r_run : m_run * c) + __builtin_amdgcn_logf(lsum)) * LN2;
+#ifdef ATTN_PHASE_TIMERS
+  // Record layout in include/attn_phase_timers.h; the exit stamp follows the issue of
+  // this wave's O and LSE stores, which complete later (as in the product build, which
+  // does not wait for them).
+  const unsigned long long rt_exit = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0 && p.timers && (int)blockIdx.x < p.timer_blocks) {
+    unsigned long long* rec =
+        p.timers + ((size_t)blockIdx.x * NW + wave) * ATTN_PHASE_TIMER_WORDS;
+    rec[0] = (unsigned long long)(n_kt > 4 ? n_kt - 4 : 0);
+    rec[1] = tm_mb;
+    rec[2] = tm_vb;
+    rec[3] = n_kt > 4 ? tm_t1 - tm_t0 : 0u;
+    rec[4] = rt_entry;
+    rec[5] = rt_loop0;
+    rec[6] = rt_loop1;
+    rec[7] = rt_exit;
+    rec[8] = (unsigned long long)n_kt;
+    rec[9] = (unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(HWREG_HW_ID) |
+             ((unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(HWREG_XCC_ID) << 32);
+  }
+#endif
 }
 
 template <bool FP8, int DQK, int BN, int NW>

@@ -26,8 +26,8 @@ struct FwdParams {
   const void* k_exact;
   int q_f32;           // FP8: q is float32, encoded on load with q's descales
 #ifdef ATTN_PHASE_TIMERS
-  // Phase-timer build only (libattn_phase_timers.so): 4 words per (workgroup, wave) of
-  // the first timer_blocks workgroups, see include/attn_phase_timers.h.
+  // Phase-timer build only (libattn_phase_timers.so): ATTN_PHASE_TIMER_WORDS words per
+  // (workgroup, wave) of the first timer_blocks workgroups, see include/attn_phase_timers.h.
   unsigned long long* timers;
   int timer_blocks;
 #endif

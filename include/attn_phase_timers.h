@@ -17,7 +17,17 @@
  *       before the barrier wait, summed;
  *   [2] the same for their softmax phases;
  *   [3] cycles from the start of the first counted tile to the start of the tile after
- *       the last one: the period, summed (so [3] - [1] - [2] is time at barriers).
+ *       the last one: the period, summed (so [3] - [1] - [2] is time at barriers);
+ *   [4] the device's real-time counter (s_memrealtime, a constant-rate clock shared by
+ *       the whole device) when the wave starts;
+ *   [5] the same when it enters its first matrix phase (Q loaded, the first two tiles'
+ *       copies issued, the first barrier passed: the prologue is [5] - [4]);
+ *   [6] the same when it leaves the key loop;
+ *   [7] the same once it has issued its O and LSE stores (the epilogue is [7] - [6]; the
+ *       stores complete afterwards, and a workgroup's CU takes the next one only then);
+ *   [8] the workgroup's key tiles (the loop runs [8] + 1 matrix phases);
+ *   [9] the wave's HW_ID register (CU in bits 8-11, shader array bit 12, shader engine
+ *       bits 13-15) in the low 32 bits and its XCC_ID register (compute die) in the high.
  * Workgroup index = launch order (the heaviest causal tiles first).  Waves 0-3 are the
  * group that starts with a matrix phase, waves 4-7 the one half a phase behind.
  */
@@ -31,7 +41,7 @@ extern "C" {
 #endif
 
 #define ATTN_PHASE_TIMER_WAVES 8
-#define ATTN_PHASE_TIMER_WORDS 4
+#define ATTN_PHASE_TIMER_WORDS 10
 
 /* Record into buf (device memory, 8-byte aligned, owned by the caller, at least
  * bytes long) from every following attention launch of this library, for the

@@ -6,6 +6,10 @@ in which every wave reads the shader clock around the two phases of each key til
 the two-group schedule (include/attn_phase_timers.h), and writes, per workload, the
 mean cycles per key tile of the matrix phase, the softmax phase and the whole period,
 per wave group, to OUTDIR/phase_timers_<workload>.txt (then copied into profiles/).
+The same records carry the device's real-time counter at each wave's start, loop entry,
+loop exit and end (its stores issued) and the wave's CU: the file's second table gives, per
+kernel, the prologue and the epilogue, the time per key tile, and the gap between one
+workgroup's end and the next one's start on the same CU, over every workgroup of the launch.
 
 Usage: python profile_phases.py [OUTDIR] [workload ...]
 (default OUTDIR gpurun_out/profiles; workloads gauss32k mla32k mistral16k)
@@ -26,8 +30,38 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-RECORD_BLOCKS = 256
-WAVES, WORDS = 8, 4           # include/attn_phase_timers.h
+PHASE_BLOCKS = 256             # workgroups summarised in the phase table
+WAVES, WORDS = 8, 10           # include/attn_phase_timers.h
+BM = 256                       # queries per workgroup (8 waves of 32)
+REALTIME_MHZ = 100.0           # rate of the device's real-time counter (checked per launch)
+
+
+def timeline(rec, event_ms):
+    """Per-kernel figures from the real-time words of every workgroup's records: prologue
+    (waves 0-3, which enter the loop first) and epilogue in µs, µs per key tile (the loop
+    of group A's waves over its tiles + 1 matrix phases), the gap between consecutive
+    workgroups on one CU, and the counter rate implied by the launch's span against its
+    event-timed duration."""
+    import numpy as np
+    used = rec[:, 0, 4] != 0
+    r = rec[used].astype(np.int64)
+    us = lambda ticks: ticks / REALTIME_MHZ
+    pro = us(r[:, 0:4, 5] - r[:, 0:4, 4]).mean()
+    epi = us(r[:, :, 7] - r[:, :, 6]).mean()
+    tile = (us(r[:, 0:4, 6] - r[:, 0:4, 5]) / (r[:, 0:4, 8] + 1)).mean()
+    start, end = r[:, :, 4].min(axis=1), r[:, :, 7].max(axis=1)
+    cu = ((r[:, 0, 9] >> 8) & 0xFF) | (((r[:, 0, 9] >> 32) & 0xFF) << 8)
+    gaps, per_cu = [], []
+    for c in np.unique(cu):
+        idx = np.where(cu == c)[0]
+        order = idx[np.argsort(start[idx])]
+        per_cu.append(len(order))
+        gaps += list(us(start[order[1:]] - end[order[:-1]]))
+    gaps = np.array(gaps) if gaps else np.zeros(1)
+    mhz = (end.max() - start.min()) / (event_ms * 1e3)
+    return {"workgroups": int(used.sum()), "cus": len(per_cu), "prologue": pro, "epilogue": epi,
+            "tile": tile, "gap_mean": float(gaps.mean()), "gap_median": float(np.median(gaps)),
+            "pairs": int(len(gaps)), "span_over_event_mhz": float(mhz)}
 
 
 def main() -> int:
@@ -41,7 +75,6 @@ def main() -> int:
     os.makedirs(out_dir, exist_ok=True)
     ba.load_library(ba.PHASE_TIMERS_LIB_PATH)
     dev = "cuda:0"
-    buf = torch.zeros(RECORD_BLOCKS * WAVES * WORDS, dtype=torch.int64, device=dev)
     command = "python profile_phases.py " + " ".join(sys.argv[1:])
 
     for name in names:
@@ -50,6 +83,8 @@ def main() -> int:
               f"d={w.d_qk}/{w.d_v})", flush=True)
         x = workloads.generate(w)
         xd = {n: torch.from_numpy(x[n]).to(dev) for n in "qkv"}
+        blocks = -(-w.N // BM) * w.B * w.Hq     # the launch's workgroups, all recorded
+        buf = torch.zeros(blocks * WAVES * WORDS, dtype=torch.int64, device=dev)
         ph = w.fp8_per_head
         nds = lambda H: (H if ph else 1)
         codes = {n: torch.empty(x[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
@@ -95,13 +130,14 @@ def main() -> int:
                  f"# command: {command}",
                  "# build: libattn_phase_timers.so (python -m bf16_causal_prefill_amd.build "
                  "--phase-timers); record layout in include/attn_phase_timers.h",
-                 f"# the first {RECORD_BLOCKS} workgroups of one launch after ~1 s of back-to-back "
+                 f"# the first {PHASE_BLOCKS} workgroups of one launch after ~1 s of back-to-back "
                  "calls; waves with >= 8 counted tiles; group A = waves 0-3 (matrix phase first)",
                  "# busy = cycles from a phase's start to its barrier; wait = period - busy(matrix) "
                  "- busy(softmax), time spent at the two barriers",
                  "",
                  f"{'kernel':52s} {'grp':>3s} {'waves':>5s} {'period':>7s} {'matrix':>7s} "
                  f"{'softmax':>7s} {'wait':>6s}"]
+        tl_rows = []
         for title, fn in kernels:
             t0 = time.time()
             while time.time() - t0 < 1.0:
@@ -111,10 +147,19 @@ def main() -> int:
             buf.zero_()
             torch.cuda.synchronize()
             ba.attn_phase_timers_set(buf)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
             fn()
+            ev1.record()
             torch.cuda.synchronize()
             ba.attn_phase_timers_set(None)
-            rec = buf.view(RECORD_BLOCKS, WAVES, WORDS).cpu().numpy()
+            rec_all = buf.view(blocks, WAVES, WORDS).cpu().numpy()
+            tl = timeline(rec_all, ev0.elapsed_time(ev1))
+            tl_rows.append(f"{title:52s} {tl['workgroups']:5d} {tl['cus']:4d} {tl['prologue']:8.2f} "
+                           f"{tl['epilogue']:8.2f} {tl['tile']:6.3f} {tl['gap_mean']:8.2f} "
+                           f"{tl['gap_median']:8.2f} {tl['span_over_event_mhz']:7.1f}")
+            print("  " + tl_rows[-1], flush=True)
+            rec = rec_all[:PHASE_BLOCKS]
             for grp, waves in (("A", range(0, 4)), ("B", range(4, 8))):
                 r = rec[:, list(waves), :].reshape(-1, WORDS)
                 r = r[r[:, 0] >= 8]
@@ -125,6 +170,16 @@ def main() -> int:
                 lines.append(f"{title:52s} {grp:>3s} {len(r):5d} {per:7.0f} {mb:7.0f} {vb:7.0f} "
                              f"{per - mb - vb:6.0f}")
             print("  " + lines[-1], flush=True)
+        lines += ["",
+                  f"# per-workgroup timeline from the real-time words, every workgroup of the "
+                  f"launch, µs at {REALTIME_MHZ:.0f} MHz: prologue = loop entry - start (waves "
+                  "0-3); epilogue = O/LSE stores issued - loop exit (all waves); tile = "
+                  "loop time / (key tiles + 1) (waves 0-3); gap = next workgroup's first wave "
+                  "start - this one's last wave end on the same CU; rate = the launch's real-time "
+                  "span over its event-timed duration (MHz, a check of the counter's rate)",
+                  "",
+                  f"{'kernel':52s} {'wgs':>5s} {'cus':>4s} {'prologue':>8s} {'epilogue':>8s} "
+                  f"{'tile':>6s} {'gap':>8s} {'gap_med':>8s} {'rate':>7s}"] + tl_rows
         path = os.path.join(out_dir, f"phase_timers_{name}.txt")
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")

@@ -49,8 +49,8 @@ def test_phase_timer_build_exports_and_validates():
     fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     fn.restype = ctypes.c_int
     assert fn(ctypes.c_void_p(A16 + 4), 4096) == ba.ATTN_E_ALIGN
-    assert fn(ctypes.c_void_p(A16), 8 * 4 * 8 - 8) == ba.ATTN_E_INVAL
-    assert fn(ctypes.c_void_p(A16), 8 * 4 * 8) == ba.ATTN_OK
+    assert fn(ctypes.c_void_p(A16), 8 * 10 * 8 - 8) == ba.ATTN_E_INVAL
+    assert fn(ctypes.c_void_p(A16), 8 * 10 * 8) == ba.ATTN_OK
     assert fn(None, 0) == ba.ATTN_OK
 
 

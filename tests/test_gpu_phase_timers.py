@@ -2,7 +2,10 @@
 runs in a child process (the package loads one library per process) on the 4K workload
 and writes a summary whose figures must be complete and consistent for every kernel
 variant and both wave groups: counted tiles present, every phase a positive number of
-cycles, and the period no shorter than the two phases' busy time."""
+cycles, and the period no shorter than the two phases' busy time; and, from the
+real-time words, every workgroup of the launch recorded, on as many CUs as the device
+has (one workgroup per CU at a time, so no negative gaps), positive prologue, epilogue
+and tile times, and the counter's rate consistent with the launch's event-timed span."""
 import os
 import subprocess
 import sys
@@ -28,13 +31,29 @@ def test_phase_timer_summary(tmp_path):
     print(r.stdout[-3000:])
     assert r.returncode == 0, r.stderr[-3000:]
     text = (tmp_path / "phase_timers_mid_gqa.txt").read_text()
+    phases, timeline = text.split("# per-workgroup timeline")
     rows = {}
-    for line in text.splitlines():
+    for line in phases.splitlines():
         if line.startswith("#") or not line.strip() or line.startswith("kernel"):
             continue
         name, rest = line[:52].strip(), line[52:].split()
         grp, waves, period, matrix, softmax, wait = rest[0], *map(float, rest[1:])
         rows[(name, grp)] = (waves, period, matrix, softmax, wait)
+    tl = {}
+    for line in timeline.splitlines()[1:]:
+        if line.startswith("#") or not line.strip() or line.startswith("kernel"):
+            continue
+        tl[line[:52].strip()] = list(map(float, line[52:].split()))
+    grid = 4096 // 256 * 32          # mid_gqa: 16 query tiles x 32 heads
+    for k in KERNELS:
+        wgs, cus, pro, epi, tile, gap, gap_med, rate = tl[k]
+        assert wgs == grid, (k, tl[k])
+        assert 128 <= cus <= 256, (k, tl[k])
+        assert pro > 0 and epi > 0 and tile > 0, (k, tl[k])
+        assert gap >= 0 and gap_med >= 0, (k, tl[k])
+        # the event-timed duration includes the launch's own latency, so the span's rate
+        # reads a little below the counter's
+        assert 70 <= rate <= 102, (k, tl[k])
     for k in KERNELS:
         for grp in "AB":
             waves, period, matrix, softmax, wait = rows[(k, grp)]

@@ -4,7 +4,8 @@ inputs both ways, quantise Q then attn_fwd_causal_fp8 on its codes, and float32 
 into attn_fwd_causal_fp8_qf32, and requires byte-identical O and LSE (NaN payloads
 included); the descales come from quantize_e4m3_qkv with q_out = None (Q's descales only),
 whose descales and K/V codes must equal the separate quantisers'.  One case per shape is
-also compared with the fp64 oracle.
+also compared with the fp64 oracle, and the full 32K workloads (gauss32k, mla32k) are
+compared byte for byte with the codes step over every workgroup of the launch.
 
 Cases: d_qk 128 with GQA and d_qk 192 (the MLA shape), a ragged N, per-tensor and per-head
 descales, Q's descale from quantize_e4m3_q_pow2 (the power-of-two softmax constant) and
@@ -101,3 +102,45 @@ def test_qf32_byte_identical(shape, per_head, q_pow2, want_lse):
     check(f"qf32-{shape}", "fp8", o_new.float().cpu().numpy().astype(np.float64), ro,
           lse_new.cpu().numpy().astype(np.float64), rl, fp8_path="exact",
           ref_abs_o=abs_v(oracle.causal_attention, qd_, kd_, vd_, scale))
+
+
+@pytest.mark.parametrize("name", ["gauss32k", "mla32k"])
+def test_qf32_full_size_byte_identical(name):
+    """The full 32K workloads (d_qk 128 with GQA, per-tensor descales; the MLA shape,
+    per-head): the float32-Q step (quantize_e4m3_qkv with Q's descales only, then
+    attn_fwd_causal_fp8_qf32) gives O and LSE byte-identical to the codes step, over every
+    workgroup of the launch."""
+    import workloads
+    w = workloads.get(name)
+    note(f"qf32 full {name}: N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk}/{w.d_v}")
+    x = workloads.generate(w)
+    xd = {n: torch.from_numpy(x[n]).to(DEV) for n in "qkv"}
+    del x
+    ph = w.fp8_per_head
+    ns = {"q": w.Hq if ph else 1, "k": w.Hkv if ph else 1, "v": w.Hkv if ph else 1}
+    codes = {n: torch.empty(xd[n].shape, device=DEV, dtype=torch.uint8) for n in "qkv"}
+    ds = {n: torch.empty((ns[n],), device=DEV) for n in "qkv"}
+    ba.quantize_e4m3_qkv(xd["q"], xd["k"], xd["v"], codes["q"], codes["k"], codes["v"], ds["q"],
+                         ds["k"], ds["v"], ph, q_pow2=True, softmax_scale=w.softmax_scale)
+    outs = []
+    for qf32 in (False, True):
+        o = torch.full((w.B, w.N, w.Hq, w.d_v), float("nan"), device=DEV, dtype=torch.bfloat16)
+        lse = torch.full((w.B, w.Hq, w.N), float("nan"), device=DEV, dtype=torch.float32)
+        if qf32:
+            dq = torch.full_like(ds["q"], float("nan"))
+            ba.quantize_e4m3_qkv(xd["q"], xd["k"], xd["v"], None, codes["k"], codes["v"], dq,
+                                 ds["k"], ds["v"], ph, q_pow2=True, softmax_scale=w.softmax_scale)
+            assert torch.equal(dq.view(torch.int32), ds["q"].view(torch.int32))
+            ba.attn_fwd_causal_fp8_qf32(xd["q"], codes["k"], codes["v"], dq, ds["k"], ds["v"],
+                                        o, lse, softmax_scale=w.softmax_scale,
+                                        descale_per_head=int(ph))
+        else:
+            ba.attn_fwd_causal_fp8(codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"],
+                                   o, lse, softmax_scale=w.softmax_scale, descale_per_head=int(ph))
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    (o0, l0), (o1, l1) = outs
+    assert not torch.isnan(o0.float()).any() and not torch.isnan(l0).any()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "O differs"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "LSE differs"
+    note("  byte-identical at full size")

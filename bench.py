@@ -476,6 +476,7 @@ def main() -> int:
     if args.copy_only:
         return copy_only(args.copy_only)
 
+    import numpy as np
     import torch
     import bf16_causal_prefill_amd as ba
     import workloads
@@ -486,6 +487,8 @@ def main() -> int:
     w = workloads.get(args.workload)
     log(f"bench: generating {w.name} inputs")
     x = workloads.generate(w)
+    # the generated float32 buffers, hashed so that a run's inputs can be checked
+    input_sha = {n: hashlib.sha256(x[n].tobytes()).hexdigest()[:16] for n in "qkv"}
     xd = {n: torch.from_numpy(x[n]).to(dev) for n in "qkv"}
     nds = lambda H: (H if w.fp8_per_head else 1)
     codes = {n: torch.empty(x[n].shape, device=dev, dtype=torch.uint8) for n in "qkv"}
@@ -660,6 +663,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
                    "d_qk": w.d_qk, "d_v": w.d_v, "inputs": "iid N(0,1) float32 in HBM",
+                   "seed": w.seed, "numpy": np.__version__, "inputs_sha256": input_sha,
                    "step": "quantize_e4m3_qkv (k, v absmax, q power-of-two scale), per "
                             "tensor, + attn_fwd_causal_fp8 (O + LSE)"},
         "pct_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),

@@ -144,3 +144,47 @@ def test_qf32_full_size_byte_identical(name):
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "O differs"
     assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "LSE differs"
     note("  byte-identical at full size")
+
+
+@pytest.mark.parametrize("case", ["inf_element", "tiny_values", "all_zero"])
+@pytest.mark.parametrize("per_head", [True, False], ids=["per_head", "per_tensor"])
+def test_qf32_descale_edges(case, per_head):
+    """Descales outside the branch-free encoder's range take the kernel's per-element
+    encoder: an infinity in Q (descale +inf: finite values encode to signed zeros, the
+    infinity to 0x7F), Q scaled by 1e-30 (descales near 2^-108), and an all-zero Q
+    (descale 1).  Byte identity with quantising Q first, absmax Q descales."""
+    B, N, Hq, Hkv, dqk, dv = 1, 300, 4, 2, 128, 128
+    note(f"qf32 edge {case} per_head={per_head}")
+    q, k, v = _inputs(B, N, Hq, Hkv, dqk, dv, 5100, False)
+    if case == "inf_element":
+        q[0, 7, 1, 3] = np.inf
+    elif case == "tiny_values":
+        q *= np.float32(1e-30)
+    else:
+        q[:] = 0.0
+    scale = 1.0 / np.sqrt(dqk)
+    dev = {n: torch.from_numpy(a).to(DEV) for n, a in (("q", q), ("k", k), ("v", v))}
+    nh = {"q": Hq if per_head else 1, "k": Hkv if per_head else 1, "v": Hkv if per_head else 1}
+    codes = {n: torch.empty(dev[n].shape, device=DEV, dtype=torch.uint8) for n in "qkv"}
+    ds = {n: torch.empty((nh[n],), device=DEV) for n in "qkv"}
+    for n in "qkv":
+        ba.quantize_e4m3(dev[n], codes[n], ds[n], per_head)
+    outs = []
+    for qf32 in (False, True):
+        o = torch.full((B, N, Hq, dv), float("nan"), device=DEV, dtype=torch.bfloat16)
+        lse = torch.full((B, Hq, N), float("nan"), device=DEV, dtype=torch.float32)
+        call = ba.attn_fwd_causal_fp8_qf32 if qf32 else ba.attn_fwd_causal_fp8
+        call(dev["q"] if qf32 else codes["q"], codes["k"], codes["v"], ds["q"], ds["k"], ds["v"],
+             o, lse, softmax_scale=scale, descale_per_head=int(per_head))
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    (o0, l0), (o1, l1) = outs
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "O differs"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "LSE differs"
+    dq = ds["q"].cpu().numpy()
+    if case == "tiny_values":
+        assert np.all(dq < 2.0 ** -100), dq          # the per-element encoder's range
+    elif case == "inf_element":
+        assert np.isinf(dq).any()
+    else:
+        assert np.all(dq == 1.0)

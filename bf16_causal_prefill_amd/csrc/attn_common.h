@@ -88,14 +88,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Maps the flat workgroup id to (batch, query head, query tile).  Heaviest causal
 // tiles (last query rows) go first.  When B*Hkv is a multiple of 8, each of the 8
 // XCDs (workgroups are dealt to XCDs round-robin) gets whole KV-head groups, so the
-// query heads that share K/V run on one XCD and share its L2.
+// query heads that share K/V run on one XCD and share its L2.  On that path the odd
+// XCD of each pair (2i, 2i+1) hands its p.xcd_swap heaviest items to the even one,
+// which runs them first, and takes the even one's p.xcd_swap lightest items, run last
+// (both keep the same number of workgroups, which round-robin dealing fixes): the odd
+// XCDs measured a few percent slower on every MI355X tried, and the launch ends with
+// its slowest XCD.
 __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
                                           int& qt) {
   const int G = p.Hq / p.Hkv;
   const int BHkv = p.B * p.Hkv;
   if ((BHkv & 7) == 0) {
-    const int xcd = bid & 7, local = bid >> 3;
+    int xcd = bid & 7, local = bid >> 3;      // local: the item's place in its XCD's list
     const int per = (BHkv >> 3) * G;
+    const int sw = p.xcd_swap;
+    if (sw > 0) {
+      const int total = p.n_qtiles * per;     // items per XCD
+      if ((xcd & 1) == 0) {
+        if (local < sw) xcd |= 1;             // the odd partner's heaviest items
+        else local -= sw;                     // then its own, less its lightest
+      } else {
+        if (local < total - sw) local += sw;  // its own, less its heaviest
+        else xcd &= ~1;                       // then the even partner's lightest
+      }
+    }
     const int t = local / per, r = local - t * per;
     qt = p.n_qtiles - 1 - t;
     const int og = r / G, hg = r - og * G;

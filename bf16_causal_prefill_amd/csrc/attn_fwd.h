@@ -1020,11 +1020,49 @@ void attn_fwd_kernel(FwdParams p) {
 #endif
 }
 
+// Items the odd XCD of each pair hands to the even one (map_block): the count whose
+// moved work, the heaviest items' key tiles less the lightest ones', comes closest to
+// XCD_SHIFT of one XCD's work, and 0 unless it lands within half of that.  XCD_SHIFT
+// = (r - 1) / (r + 1) for an odd/even time ratio r = 1.03 at equal work, the low end of
+// what the phase-timer build measured (1.027-1.048 over four boxes, every kernel and
+// size; rotating the KV heads over the XCDs left the odd XCDs the slow ones).
+constexpr double XCD_SHIFT = 0.03 / 2.03;
+
+template <int BM, int BN>
+static int xcd_swap_count(const FwdParams& p) {
+  const int BHkv = p.B * p.Hkv;
+  if ((BHkv & 7) != 0) return 0;
+  const int per = (BHkv >> 3) * (p.Hq / p.Hkv);
+  const long long total = (long long)p.n_qtiles * per;
+  // key tiles of the items in row t of an XCD's list (query tile n_qtiles - 1 - t)
+  auto row_weight = [&](long long t) -> long long {
+    const long long qt = p.n_qtiles - 1 - t;
+    const long long wg_end = qt * BM + BM < p.Nq ? qt * BM + BM : p.Nq;
+    const long long keys = wg_end + p.q_off < p.Nk ? wg_end + p.q_off : p.Nk;
+    return (keys + BN - 1) / BN;
+  };
+  long long work = 0;
+  for (long long t = 0; t < p.n_qtiles; ++t) work += per * row_weight(t);
+  const double target = XCD_SHIFT * (double)work;
+  long long moved = 0, best = 0;
+  double best_err = target;
+  for (long long s = 1; s <= total / 2; ++s) {
+    const long long gain = row_weight((s - 1) / per) - row_weight((total - s) / per);
+    if (gain <= 0) break;                    // items are in falling weight
+    moved += gain;
+    const double err = moved > target ? moved - target : target - moved;
+    if (err < best_err) { best_err = err; best = s; }
+    if (moved > target) break;
+  }
+  return best_err <= 0.5 * target ? (int)best : 0;
+}
+
 template <bool FP8, int DQK, int BN, int NW>
 static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   using C = Cfg<FP8, DQK, BN, NW>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
+  p.xcd_swap = xcd_swap_count<C::BM, BN>(p);
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, false>

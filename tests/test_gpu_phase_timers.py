@@ -5,7 +5,7 @@ variant and both wave groups: counted tiles present, every phase a positive numb
 cycles, and the period no shorter than the two phases' busy time; and, from the
 real-time words, every workgroup of the launch recorded, on as many CUs as the device
 has (one workgroup per CU at a time, so no negative gaps), positive prologue, epilogue
-and tile times, and the counter's rate consistent with the launch's event-timed span."""
+and tile times, and the counter's rate no higher than the launch's event-timed span allows."""
 import os
 import subprocess
 import sys
@@ -51,9 +51,11 @@ def test_phase_timer_summary(tmp_path):
         assert 128 <= cus <= 256, (k, tl[k])
         assert pro > 0 and epi > 0 and tile > 0, (k, tl[k])
         assert gap >= 0 and gap_med >= 0, (k, tl[k])
-        # the event-timed duration includes the launch's own latency, so the span's rate
-        # reads a little below the counter's
-        assert 70 <= rate <= 102, (k, tl[k])
+        # the event-timed duration includes the launch's own latency (tens of µs at times,
+        # against a 4K launch's ~75 µs), so the span's rate reads below the counter's
+        # 100 MHz, never above it; the floor only catches a counter off by an order of
+        # magnitude (the 16K and 32K launches read 98-99.7 MHz)
+        assert 20 <= rate <= 102, (k, tl[k])
     for k in KERNELS:
         for grp in "AB":
             waves, period, matrix, softmax, wait = rows[(k, grp)]

@@ -89,11 +89,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // tiles (last query rows) go first.  When B*Hkv is a multiple of 8, each of the 8
 // XCDs (workgroups are dealt to XCDs round-robin) gets whole KV-head groups, so the
 // query heads that share K/V run on one XCD and share its L2.  On that path the odd
-// XCD of each pair (2i, 2i+1) hands its p.xcd_swap heaviest items to the even one,
-// which runs them first, and takes the even one's p.xcd_swap lightest items, run last
-// (both keep the same number of workgroups, which round-robin dealing fixes): the odd
-// XCDs measured a few percent slower on every MI355X tried, and the launch ends with
-// its slowest XCD.
+// XCD of each pair (2i, 2i+1) hands its sw = p.xcd_swap heaviest items to the even
+// one, which runs them first, and takes the even one's items at places j .. j+sw-1 of
+// its list (j = p.xcd_swap_at >= sw, lighter ones), run where their weight puts them:
+// both keep the same number of workgroups, which round-robin dealing fixes.  The odd
+// XCDs measured a few percent slower on every MI355X tried, and a launch ends with its
+// slowest XCD.
 __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
                                           int& qt) {
   const int G = p.Hq / p.Hkv;
@@ -101,15 +102,18 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, i
   if ((BHkv & 7) == 0) {
     int xcd = bid & 7, local = bid >> 3;      // local: the item's place in its XCD's list
     const int per = (BHkv >> 3) * G;
-    const int sw = p.xcd_swap;
+    const int sw = p.xcd_swap, j = p.xcd_swap_at;
     if (sw > 0) {
-      const int total = p.n_qtiles * per;     // items per XCD
       if ((xcd & 1) == 0) {
-        if (local < sw) xcd |= 1;             // the odd partner's heaviest items
-        else local -= sw;                     // then its own, less its lightest
+        if (local < sw) xcd |= 1;             // the odd partner's heaviest items,
+        else if (local < j + sw) local -= sw; // then its own before place j,
+                                              // then its own after place j + sw - 1
       } else {
-        if (local < total - sw) local += sw;  // its own, less its heaviest
-        else xcd &= ~1;                       // then the even partner's lightest
+        if (local < j - sw) local += sw;      // its own after its sw heaviest,
+        else if (local < j) {                 // then the even partner's j .. j+sw-1,
+          xcd &= ~1;
+          local += sw;
+        }                                     // then its own from place j
       }
     }
     const int t = local / per, r = local - t * per;

@@ -54,6 +54,7 @@
 #include <stdint.h>
 
 
+#include <cmath>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1020,41 +1021,72 @@ void attn_fwd_kernel(FwdParams p) {
 #endif
 }
 
-// Items the odd XCD of each pair hands to the even one (map_block): the count whose
-// moved work, the heaviest items' key tiles less the lightest ones', comes closest to
-// XCD_SHIFT of one XCD's work, and 0 unless it lands within half of that.  XCD_SHIFT
-// = (r - 1) / (r + 1) for an odd/even time ratio r = 1.03 at equal work, the low end of
-// what the phase-timer build measured (1.027-1.048 over four boxes, every kernel and
-// size; rotating the KV heads over the XCDs left the odd XCDs the slow ones).
+// The exchange between the XCDs of a pair (map_block): the odd XCD hands its sw
+// heaviest items to the even one for the even one's items at places j .. j+sw-1, so
+// that the moved work, in key tiles, comes closest to XCD_SHIFT of one XCD's work: the
+// fewest items that can move that much, and the block of the even XCD's list whose
+// weight leaves the closest difference; none unless it lands within half of the target.
+// XCD_SHIFT = (r - 1) / (r + 1) for an odd/even time ratio r = 1.03 at equal work, the
+// low end of what the phase-timer build measured (1.027-1.048 over five boxes, every
+// kernel and size; rotating the KV heads over the XCDs left the odd XCDs the slow ones).
 constexpr double XCD_SHIFT = 0.03 / 2.03;
+// Only with at least this many items per CU of an XCD (32 CUs each on MI355X): with two
+// (4K, B=1) one traded item upset the balance between the XCD's own CUs, and the
+// exchange cost 3-4% there instead of gaining.
+constexpr long long XCD_SWAP_MIN_ITEMS = 6 * 32;
 
 template <int BM, int BN>
-static int xcd_swap_count(const FwdParams& p) {
+static void xcd_swap_plan(FwdParams& p) {
+  p.xcd_swap = 0;
+  p.xcd_swap_at = 0;
   const int BHkv = p.B * p.Hkv;
-  if ((BHkv & 7) != 0) return 0;
-  const int per = (BHkv >> 3) * (p.Hq / p.Hkv);
+  if ((BHkv & 7) != 0) return;
+  const long long per = (long long)(BHkv >> 3) * (p.Hq / p.Hkv);
   const long long total = (long long)p.n_qtiles * per;
-  // key tiles of the items in row t of an XCD's list (query tile n_qtiles - 1 - t)
-  auto row_weight = [&](long long t) -> long long {
-    const long long qt = p.n_qtiles - 1 - t;
+  if (total < XCD_SWAP_MIN_ITEMS) return;
+  // key tiles of the item at place i of an XCD's list (query tile n_qtiles - 1 - i/per)
+  auto w = [&](long long i) -> long long {
+    const long long qt = p.n_qtiles - 1 - i / per;
     const long long wg_end = qt * BM + BM < p.Nq ? qt * BM + BM : p.Nq;
     const long long keys = wg_end + p.q_off < p.Nk ? wg_end + p.q_off : p.Nk;
     return (keys + BN - 1) / BN;
   };
   long long work = 0;
-  for (long long t = 0; t < p.n_qtiles; ++t) work += per * row_weight(t);
+  for (long long t = 0; t < p.n_qtiles; ++t) work += per * w(t * per);
   const double target = XCD_SHIFT * (double)work;
-  long long moved = 0, best = 0;
-  double best_err = target;
-  for (long long s = 1; s <= total / 2; ++s) {
-    const long long gain = row_weight((s - 1) / per) - row_weight((total - s) / per);
-    if (gain <= 0) break;                    // items are in falling weight
-    moved += gain;
-    const double err = moved > target ? moved - target : target - moved;
-    if (err < best_err) { best_err = err; best = s; }
-    if (moved > target) break;
+  long long heavy = 0, light = 0;
+  for (long long s = 1; 2 * s <= total; ++s) {
+    // the most s items can move: the s heaviest for the s lightest; once one more pair
+    // moves nothing (falling weights), no larger s moves more
+    if (w(s - 1) <= w(total - s)) return;
+    heavy += w(s - 1);
+    light += w(total - s);
+    if ((double)(heavy - light) < target) continue;
+    // blocks get lighter as j grows: take the first j whose block moves at least the
+    // target, or the one before it if that comes closer
+    long long lo = s, hi = total - s;         // block(lo) heaviest, block(hi) lightest
+    auto block = [&](long long jj) {
+      long long b = 0;
+      for (long long i = jj; i < jj + s; ++i) b += w(i);
+      return b;
+    };
+    const double need = (double)heavy - target;
+    while (lo < hi) {                         // first j with block(j) <= need
+      const long long mid = (lo + hi) / 2;
+      if ((double)block(mid) <= need) hi = mid; else lo = mid + 1;
+    }
+    long long jb = lo;
+    double err = std::fabs((double)(heavy - block(jb)) - target);
+    if (jb > s) {
+      const double e2 = std::fabs((double)(heavy - block(jb - 1)) - target);
+      if (e2 < err) { err = e2; jb -= 1; }
+    }
+    if (err <= 0.5 * target) {
+      p.xcd_swap = (int)s;
+      p.xcd_swap_at = (int)jb;
+    }
+    return;
   }
-  return best_err <= 0.5 * target ? (int)best : 0;
 }
 
 template <bool FP8, int DQK, int BN, int NW>
@@ -1062,7 +1094,7 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   using C = Cfg<FP8, DQK, BN, NW>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
-  p.xcd_swap = xcd_swap_count<C::BM, BN>(p);
+  xcd_swap_plan<C::BM, BN>(p);
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, false>

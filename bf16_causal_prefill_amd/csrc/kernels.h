@@ -25,7 +25,8 @@ struct FwdParams {
   const void* q_exact; // from these bf16 side arrays (B, Nq, Hq, 32) and (B, Nk, Hkv, 32)
   const void* k_exact;
   int q_f32;           // FP8: q is float32, encoded on load with q's descales
-  int xcd_swap;        // items each odd XCD trades with its even partner (the launcher)
+  int xcd_swap;        // items each odd XCD trades with its even partner, and the place
+  int xcd_swap_at;     // in the even one's list of the items it takes (the launcher)
 #ifdef ATTN_PHASE_TIMERS
   // Phase-timer build only (libattn_phase_timers.so): ATTN_PHASE_TIMER_WORDS words per
   // (workgroup, wave) of the first timer_blocks workgroups, see include/attn_phase_timers.h.

@@ -94,7 +94,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // its list (j = p.xcd_swap_at >= sw, lighter ones), run where their weight puts them:
 // both keep the same number of workgroups, which round-robin dealing fixes.  The odd
 // XCDs measured a few percent slower on every MI355X tried, and a launch ends with its
-// slowest XCD.
+// slowest XCD.  Within an XCD, workgroups are dealt in order to its 4 shader engines,
+// place k to engine (k mod 4) (a fixed order per XCD, measured), and a workgroup waits
+// for a free CU on its own engine.  With p.se_rotate each group of 4 consecutive places
+// takes the group's 4 items rotated by the group index, so every engine gets, over 4
+// groups, every position of a group (the heavier and the lighter row when a row has
+// fewer than 4 items, every head of a KV group when it has 4) instead of always the
+// same one; the launcher sets it for the FP8 kernels without the exact LSE, the ones it
+// measured faster.
 __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
                                           int& qt) {
   const int G = p.Hq / p.Hkv;
@@ -102,6 +109,10 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, i
   if ((BHkv & 7) == 0) {
     int xcd = bid & 7, local = bid >> 3;      // local: the item's place in its XCD's list
     const int per = (BHkv >> 3) * G;
+    if (p.se_rotate) {
+      const int grp = local >> 2;
+      if (4 * grp + 4 <= p.n_qtiles * per) local = 4 * grp + (((local & 3) + grp) & 3);
+    }
     const int sw = p.xcd_swap, j = p.xcd_swap_at;
     if (sw > 0) {
       if ((xcd & 1) == 0) {

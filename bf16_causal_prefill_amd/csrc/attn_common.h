@@ -100,8 +100,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // takes the group's 4 items rotated by the group index, so every engine gets, over 4
 // groups, every position of a group (the heavier and the lighter row when a row has
 // fewer than 4 items, every head of a KV group when it has 4) instead of always the
-// same one; the launcher sets it for the FP8 kernels without the exact LSE, the ones it
-// measured faster.
+// same one; the launcher sets it for the FP8 kernels, except for the exact-LSE one when
+// a row has 4 or more items: the cases it measured faster.
 __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
                                           int& qt) {
   const int G = p.Hq / p.Hkv;

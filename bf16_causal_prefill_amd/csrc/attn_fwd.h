@@ -1096,9 +1096,12 @@ static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
   xcd_swap_plan<C::BM, BN>(p);
   // Same-box A/B of the shader-engine rotation (map_block), four alternations on each of
-  // two boxes: FP8 without the LSE +0.4% to +1.9% on every shape; BF16 -0.2% to -0.65%
-  // and FP8 with the exact LSE -0.75% to +0.4%, so only the former use it.
-  p.se_rotate = FP8 && (!p.lse || p.lse_rounded) ? 1 : 0;
+  // two boxes: FP8 without the LSE +0.4% to +1.9% on every shape; BF16 -0.2% to -0.65%;
+  // FP8 with the exact LSE +0.3% and +0.4% where a row of the XCD's list has fewer than 4
+  // items (mla32k: the lighter row of each pair always fell to the same two engines) and
+  // -0.75% to -0.1% where it has 4 (only the heads rotate then).
+  const int row_items = (p.B * p.Hkv) % 8 == 0 ? (p.B * p.Hkv / 8) * (p.Hq / p.Hkv) : 0;
+  p.se_rotate = FP8 && (!p.lse || p.lse_rounded || (row_items > 0 && row_items < 4)) ? 1 : 0;
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, false>

@@ -9,7 +9,9 @@ per wave group, to OUTDIR/phase_timers_<workload>.txt (then copied into profiles
 The same records carry the device's real-time counter at each wave's start, loop entry,
 loop exit and end (its stores issued) and the wave's CU: the file's second table gives, per
 kernel, the prologue and the epilogue, the time per key tile, and the gap between one
-workgroup's end and the next one's start on the same CU, over every workgroup of the launch.
+workgroup's end and the next one's start on the same CU, over every workgroup of the launch;
+a third table gives the balance over the 8 XCDs (busy time per CU of each, odd over even)
+and the gaps per shader engine.
 
 Usage: python profile_phases.py [OUTDIR] [workload ...]
 (default OUTDIR gpurun_out/profiles; workloads gauss32k mla32k mistral16k)
@@ -59,9 +61,27 @@ def timeline(rec, event_ms):
         gaps += list(us(start[order[1:]] - end[order[:-1]]))
     gaps = np.array(gaps) if gaps else np.zeros(1)
     mhz = (end.max() - start.min()) / (event_ms * 1e3)
+    # balance: busy µs per CU of each XCD (from XCC_ID), and the mean gap per shader engine
+    # (HW_ID bits 13-15) over all XCDs
+    xcc = (r[:, 0, 9] >> 32) & 0xF
+    se = (r[:, 0, 9] >> 13) & 0x7
+    busy = [float(us(end - start)[xcc == x].sum()) / max(1, len(np.unique(cu[xcc == x])))
+            for x in range(8)]
+    se_gap = []
+    for e in range(4):
+        g = []
+        for c in np.unique(cu[se == e]):
+            idx = np.where(cu == c)[0]
+            order = idx[np.argsort(start[idx])]
+            g += list(us(start[order[1:]] - end[order[:-1]]))
+        se_gap.append(float(np.mean(g)) if g else 0.0)
+    even, odd = np.mean(busy[0::2]), np.mean(busy[1::2])
     return {"workgroups": int(used.sum()), "cus": len(per_cu), "prologue": pro, "epilogue": epi,
             "tile": tile, "gap_mean": float(gaps.mean()), "gap_median": float(np.median(gaps)),
-            "pairs": int(len(gaps)), "span_over_event_mhz": float(mhz)}
+            "pairs": int(len(gaps)), "span_over_event_mhz": float(mhz),
+            "xcd_busy": busy, "odd_over_even": float(odd / even) if even > 0 else 0.0,
+            "span_over_mean_xcd": float(us(end.max() - start.min()) / np.mean(busy)),
+            "se_gap": se_gap}
 
 
 def main() -> int:
@@ -137,7 +157,7 @@ def main() -> int:
                  "",
                  f"{'kernel':52s} {'grp':>3s} {'waves':>5s} {'period':>7s} {'matrix':>7s} "
                  f"{'softmax':>7s} {'wait':>6s}"]
-        tl_rows = []
+        tl_rows, bal_rows = [], []
         for title, fn in kernels:
             t0 = time.time()
             while time.time() - t0 < 1.0:
@@ -159,6 +179,9 @@ def main() -> int:
                            f"{tl['epilogue']:8.2f} {tl['tile']:6.3f} {tl['gap_mean']:8.2f} "
                            f"{tl['gap_median']:8.2f} {tl['span_over_event_mhz']:7.1f}")
             print("  " + tl_rows[-1], flush=True)
+            bal_rows.append(f"{title:52s} " + " ".join(f"{b:6.0f}" for b in tl["xcd_busy"]) +
+                            f" {tl['odd_over_even']:7.4f} {tl['span_over_mean_xcd']:7.4f}  " +
+                            " ".join(f"{g:5.2f}" for g in tl["se_gap"]))
             rec = rec_all[:PHASE_BLOCKS]
             for grp, waves in (("A", range(0, 4)), ("B", range(4, 8))):
                 r = rec[:, list(waves), :].reshape(-1, WORDS)
@@ -180,6 +203,14 @@ def main() -> int:
                   "",
                   f"{'kernel':52s} {'wgs':>5s} {'cus':>4s} {'prologue':>8s} {'epilogue':>8s} "
                   f"{'tile':>6s} {'gap':>8s} {'gap_med':>8s} {'rate':>7s}"] + tl_rows
+        lines += ["",
+                  "# balance over the dies and shader engines, same launches: busy µs per CU of each "
+                  "XCD (XCC_ID 0-7), the odd XCDs' mean over the even ones', the launch's span over "
+                  "the mean XCD's busy time, and the mean gap (µs) between workgroups on one CU per "
+                  "shader engine 0-3 (HW_ID bits 13-15)",
+                  "",
+                  f"{'kernel':52s} " + " ".join(f"{'xcd' + str(x):>6s}" for x in range(8)) +
+                  f" {'odd/ev':>7s} {'span/m':>7s}  " + " ".join(f"{'se' + str(e):>5s}" for e in range(4))] + bal_rows
         path = os.path.join(out_dir, f"phase_timers_{name}.txt")
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")

@@ -5,7 +5,9 @@ variant and both wave groups: counted tiles present, every phase a positive numb
 cycles, and the period no shorter than the two phases' busy time; and, from the
 real-time words, every workgroup of the launch recorded, on as many CUs as the device
 has (one workgroup per CU at a time, so no negative gaps), positive prologue, epilogue
-and tile times, and the counter's rate no higher than the launch's event-timed span allows."""
+and tile times, and the counter's rate no higher than the launch's event-timed span allows;
+and the balance table: every XCD busy, the odd/even ratio within 20%, the span no shorter
+than the mean XCD's busy time, non-negative gaps on every shader engine."""
 import os
 import subprocess
 import sys
@@ -31,7 +33,8 @@ def test_phase_timer_summary(tmp_path):
     print(r.stdout[-3000:])
     assert r.returncode == 0, r.stderr[-3000:]
     text = (tmp_path / "phase_timers_mid_gqa.txt").read_text()
-    phases, timeline = text.split("# per-workgroup timeline")
+    phases, rest = text.split("# per-workgroup timeline")
+    timeline, balance = rest.split("# balance over")
     rows = {}
     for line in phases.splitlines():
         if line.startswith("#") or not line.strip() or line.startswith("kernel"):
@@ -56,6 +59,17 @@ def test_phase_timer_summary(tmp_path):
         # 100 MHz, never above it; the floor only catches a counter off by an order of
         # magnitude (the 16K and 32K launches read 98-99.7 MHz)
         assert 20 <= rate <= 102, (k, tl[k])
+    bal = {}
+    for line in balance.splitlines()[1:]:
+        if line.startswith("#") or not line.strip() or line.startswith("kernel"):
+            continue
+        bal[line[:52].strip()] = list(map(float, line[52:].split()))
+    for k in KERNELS:
+        busy, ratio, span_m, se_gap = bal[k][:8], bal[k][8], bal[k][9], bal[k][10:]
+        assert len(se_gap) == 4 and all(b > 0 for b in busy), (k, bal[k])
+        # the XCDs differ by a few percent; the launch cannot end before its mean XCD
+        assert 0.8 < ratio < 1.25 and span_m >= 0.99, (k, bal[k])
+        assert all(g >= 0 for g in se_gap), (k, bal[k])
     for k in KERNELS:
         for grp in "AB":
             waves, period, matrix, softmax, wait = rows[(k, grp)]

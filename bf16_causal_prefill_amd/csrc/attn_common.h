@@ -102,8 +102,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // fewer than 4 items, every head of a KV group when it has 4) instead of always the
 // same one; the launcher sets it for the FP8 kernels, except for the exact-LSE one when
 // a row has 4 or more items: the cases it measured faster.
-__device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
-                                          int& qt) {
+__host__ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& b, int& h,
+                                                   int& qt) {
   const int G = p.Hq / p.Hkv;
   const int BHkv = p.B * p.Hkv;
   if ((BHkv & 7) == 0) {

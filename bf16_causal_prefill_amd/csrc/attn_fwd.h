@@ -1089,19 +1089,26 @@ static void xcd_swap_plan(FwdParams& p) {
   }
 }
 
+// The tile map's parameters for one launch (p.n_qtiles set): the XCD pair exchange and
+// the shader-engine rotation (map_block).
+template <bool FP8, int BM, int BN>
+static void schedule_tiles(FwdParams& p) {
+  xcd_swap_plan<BM, BN>(p);
+  // Same-box A/B of the shader-engine rotation, four alternations on each of two boxes:
+  // FP8 without the LSE +0.4% to +1.9% on every shape; BF16 -0.2% to -0.65%; FP8 with the
+  // exact LSE +0.3% and +0.4% where a row of the XCD's list has fewer than 4 items
+  // (mla32k: the lighter row of each pair always fell to the same two engines) and
+  // -0.75% to -0.1% where it has 4 (only the heads rotate then).
+  const int row_items = (p.B * p.Hkv) % 8 == 0 ? (p.B * p.Hkv / 8) * (p.Hq / p.Hkv) : 0;
+  p.se_rotate = FP8 && (!p.lse || p.lse_rounded || (row_items > 0 && row_items < 4)) ? 1 : 0;
+}
+
 template <bool FP8, int DQK, int BN, int NW>
 static hipError_t launch_cfg(const FwdParams& p0, hipStream_t stream) {
   using C = Cfg<FP8, DQK, BN, NW>;
   FwdParams p = p0;
   p.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
-  xcd_swap_plan<C::BM, BN>(p);
-  // Same-box A/B of the shader-engine rotation (map_block), four alternations on each of
-  // two boxes: FP8 without the LSE +0.4% to +1.9% on every shape; BF16 -0.2% to -0.65%;
-  // FP8 with the exact LSE +0.3% and +0.4% where a row of the XCD's list has fewer than 4
-  // items (mla32k: the lighter row of each pair always fell to the same two engines) and
-  // -0.75% to -0.1% where it has 4 (only the heads rotate then).
-  const int row_items = (p.B * p.Hkv) % 8 == 0 ? (p.B * p.Hkv / 8) * (p.Hq / p.Hkv) : 0;
-  p.se_rotate = FP8 && (!p.lse || p.lse_rounded || (row_items > 0 && row_items < 4)) ? 1 : 0;
+  schedule_tiles<FP8, C::BM, BN>(p);
   const long long grid = (long long)p.n_qtiles * p.B * p.Hq;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto kern = !p.lse ? attn_fwd_kernel<FP8, DQK, BN, NW, 0, false, false>

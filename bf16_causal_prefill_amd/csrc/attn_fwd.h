@@ -149,7 +149,11 @@ void attn_fwd_kernel(FwdParams p) {
   const int hkv = h / (p.Hq / p.Hkv);
   const int Nq = p.Nq, Nk = p.Nk, q_off = p.q_off;
   const int q0 = qt * C::BM;
-  const int q0w = q0 + wave * 32;
+  // With late_rows_ahead, waves 0..NW/2-1 (group A, half a phase ahead in the key loop)
+  // own the later half of the rows. The group that ends the loop last then has no key in
+  // the last tile, so the loop ends with the leading group's masked softmax and last P V,
+  // not with a softmax and a P V after it.
+  const int q0w = q0 + (p.late_rows_ahead ? wave ^ (NW / 2) : wave) * 32;
 
   const size_t kstride = (size_t)p.Hkv * DQK * C::EB;   // bytes between keys
   const size_t vstride = (size_t)p.Hkv * DV * C::EB;
@@ -928,7 +932,10 @@ void attn_fwd_kernel(FwdParams p) {
   // unchanged).  Peeling the fill puts a second copy of the softmax phase outside the
   // loop; in the two exact-LSE kernels nearest the 256-VGPR limit (the exact channels,
   // and d192 with float32 Q) that made the register allocator spill, so they keep the
-  // fill inside the loop (with all its slots) and peel only the drain.
+  // fill inside the loop (with all its slots) and peel only the drain.  A wave whose
+  // rows see no key of the last tile (w_kt < n_kt: the first half of the workgroup's
+  // rows when the tile crosses their diagonal) has a zero P(n_kt - 1) and skips the
+  // drain's P V; it still issues its share of the (unused) copy, as every phase does.
   constexpr bool PEEL_FILL = !(EXACT && (SPLIT || (QF32 && DQK == 192)));
 #ifdef ATTN_PHASE_TIMERS
   // Measurement build: shader-clock reads around each phase of the tiles past the
@@ -968,7 +975,12 @@ void attn_fwd_kernel(FwdParams p) {
     wait_vmcnt<NDMA>();                      \
     phase_barrier();                         \
   }                                          \
-  mfma_phase(n_kt, std::integral_constant<int, 2>{}); \
+  if (w_kt == n_kt) {                        \
+    mfma_phase(n_kt, std::integral_constant<int, 2>{}); \
+  } else {                                   \
+    __builtin_amdgcn_s_setprio(1);           \
+    copy_tile(n_kt + 2);                     \
+  }                                          \
   wait_vmcnt<NDMA>();                        \
   phase_barrier();
   if constexpr (EXACT) {
@@ -1137,6 +1149,11 @@ static void schedule_tiles(FwdParams& p) {
   // -0.75% to -0.1% where it has 4 (only the heads rotate then).
   const int row_items = (p.B * p.Hkv) % 8 == 0 ? (p.B * p.Hkv / 8) * (p.Hq / p.Hkv) : 0;
   p.se_rotate = FP8 && (!p.lse || p.lse_rounded || (row_items > 0 && row_items < 4)) ? 1 : 0;
+  // Later rows in the leading wave group: same-box A/B, outputs unchanged, at 4K (2 query
+  // tiles per CU) +0.5% to +1.1% for every kernel; at 8 and 16 per CU (mla32k, gauss32k)
+  // -0.4% to +0.9% with FP8 and the exact LSE at gauss32k consistently -0.4%.  So only
+  // launches with at most 4 query tiles per CU (256 CUs) use it.
+  p.late_rows_ahead = (long long)p.n_qtiles * p.B * p.Hq <= 4LL * 256 ? 1 : 0;
 }
 
 template <bool FP8, int DQK, int BN, int NW>

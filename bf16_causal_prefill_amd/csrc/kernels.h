@@ -28,6 +28,7 @@ struct FwdParams {
   int xcd_swap;        // items each odd XCD trades with its even partner, and the place
   int xcd_swap_at;     // in the even one's list of the items it takes (the launcher)
   int se_rotate;       // rotate items over each XCD's shader engines (the launcher)
+  int late_rows_ahead; // the wave group ahead in the key loop owns the later rows (the launcher)
 #ifdef ATTN_PHASE_TIMERS
   // Phase-timer build only (libattn_phase_timers.so): ATTN_PHASE_TIMER_WORDS words per
   // (workgroup, wave) of the first timer_blocks workgroups, see include/attn_phase_timers.h.

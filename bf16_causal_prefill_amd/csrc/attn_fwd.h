@@ -160,34 +160,16 @@ void attn_fwd_kernel(FwdParams p) {
   const char* kbase = (const char*)p.k + ((size_t)b * Nk * p.Hkv + hkv) * DQK * C::EB;
   const char* vbase = (const char*)p.v + ((size_t)b * Nk * p.Hkv + hkv) * DV * C::EB;
 
-  // Softmax constant in log2 units per raw score unit (descales folded in for FP8).
+  // Softmax constant in log2 units per raw score unit (descales folded in for FP8), V's
+  // descale, Q's descale, and the power-of-two form of c (below).  They are set after the
+  // Q loads and the first tile's copy are issued: the descales are memory loads, and the
+  // decision on c branches, so taking them first put a second memory round trip in front
+  // of the Q and K/V loads of every workgroup.
   float c = p.scale * LOG2E;
   float vds = 1.f;
   float dq = 1.f;   // FP8: Q's descale (float32 Q is encoded with it in the prologue)
-  if (FP8) {
-    dq = p.qds[p.per_head ? h : 0];
-    const float dk = p.kds[p.per_head ? hkv : 0];
-    vds = p.vds[p.per_head ? hkv : 0];
-    c *= dq * dk;
-  }
-  // FP8 with the exact LSE, c within 4 ulps of a power of two 2^ce (a relative change
-  // below 2^-21, the size of the rounding already in c's float32 product; a Q descale
-  // chosen for it makes this the case): the Q operand's E8M0 scale applies c inside the
-  // matrix instruction and its first k-step starts from -r_run, the running max in log2
-  // units, so the scores leave the MFMA as the exponent arguments themselves and the
-  // softmax phase needs no FMA per score.  Otherwise qsc is 1.0 and init16 stays zero.
   bool P2 = false;
   int qsc = 0x7f7f7f7f;   // E8M0 scale of the Q operand, one byte per 32-element block
-  if constexpr (EXACT) {
-    const uint32_t cb = __float_as_uint(c);
-    const uint32_t man = cb & 0x7fffffu;
-    const int ce = (int)((cb >> 23) & 0xffu) - 127 + (man >= 0x400000u ? 1 : 0);
-    P2 = ((cb >> 23) & 0xffu) != 0u && ((cb >> 23) & 0xffu) != 0xffu &&
-         (man <= 4u || man >= 0x7ffffcu) && ce >= -120 && ce <= 120;
-    // with exact channels, 2^ce also scales their bf16 Q values: keep those normal
-    if (SPLIT) P2 = P2 && ce >= -100 && ce <= 100;
-    if (P2) qsc = (127 + ce) * 0x01010101;
-  }
 
   // ---- Q^T fragments (B operand), held for the whole key loop -------------------
   // Rows past Nq read row Nq-1 (finite data); their outputs are never stored.
@@ -231,20 +213,13 @@ void attn_fwd_kernel(FwdParams p) {
         for (int e = 0; e < 8; ++e) qf[C::KS - 1][e] = 0;
       }
       // BF16 k-step sk: lane (query l32, half g) holds exact channels 16sk+8g .. +7 of its
-      // row of q_exact.  On the power-of-two path the Q operand's scale 2^ce applies to
-      // the FP8 products, so the bf16 values carry it too (exact unless it leaves bf16's
-      // normal range, which the bound on ce keeps away from the values quantisation
-      // produces).
-      const float qmul = P2 ? __uint_as_float((uint32_t)(qsc & 0xff) << 23) : 1.f;   // 2^ce
+      // row of q_exact.  On the power-of-two path they are scaled by 2^ce further down,
+      // once c is known (exact unless it leaves bf16's normal range, which the bound on
+      // ce keeps away from the values quantisation produces).
       const __bf16* xrow = (const __bf16*)p.q_exact +
                            ((size_t)((size_t)b * Nq + qrow) * p.Hq + h) * NSPC;
 #pragma unroll
-      for (int sk = 0; sk < NSPC / 16; ++sk) {
-        bf16x8 v = *(const bf16x8*)(xrow + 16 * sk + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * qmul);
-        qsp[sk] = v;
-      }
+      for (int sk = 0; sk < NSPC / 16; ++sk) qsp[sk] = *(const bf16x8*)(xrow + 16 * sk + 8 * g);
     }
   }
 
@@ -881,6 +856,39 @@ void attn_fwd_kernel(FwdParams p) {
   // would sink the P V MFMAs into a branch that followed them).
   zero_p();                             // the first matrix phase has no P yet
   copy_tile(0);
+  if (FP8) {
+    dq = p.qds[p.per_head ? h : 0];
+    const float dk = p.kds[p.per_head ? hkv : 0];
+    vds = p.vds[p.per_head ? hkv : 0];
+    c *= dq * dk;
+  }
+  // FP8 with the exact LSE, c within 4 ulps of a power of two 2^ce (a relative change
+  // below 2^-21, the size of the rounding already in c's float32 product; a Q descale
+  // chosen for it makes this the case): the Q operand's E8M0 scale applies c inside the
+  // matrix instruction and its first k-step starts from -r_run, the running max in log2
+  // units, so the scores leave the MFMA as the exponent arguments themselves and the
+  // softmax phase needs no FMA per score.  Otherwise qsc is 1.0 and init16 stays zero.
+  if constexpr (EXACT) {
+    const uint32_t cb = __float_as_uint(c);
+    const uint32_t man = cb & 0x7fffffu;
+    const int ce = (int)((cb >> 23) & 0xffu) - 127 + (man >= 0x400000u ? 1 : 0);
+    P2 = ((cb >> 23) & 0xffu) != 0u && ((cb >> 23) & 0xffu) != 0xffu &&
+         (man <= 4u || man >= 0x7ffffcu) && ce >= -120 && ce <= 120;
+    // with exact channels, 2^ce also scales their bf16 Q values: keep those normal
+    if (SPLIT) P2 = P2 && ce >= -100 && ce <= 100;
+    if (P2) qsc = (127 + ce) * 0x01010101;
+  }
+  if constexpr (SPLIT) {
+    // On the power-of-two path the Q operand's scale 2^ce applies to the FP8 products, so
+    // the exact channels' bf16 Q values carry it too.
+    if (P2) {
+      const float qmul = __uint_as_float((uint32_t)(qsc & 0xff) << 23);   // 2^ce
+#pragma unroll
+      for (int sk = 0; sk < NSPC / 16; ++sk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qsp[sk][e] = (__bf16)((float)qsp[sk][e] * qmul);
+    }
+  }
   if constexpr (QF32) {
     // The codes quantize_e4m3 / quantize_e4m3_q_pow2 write with this descale (round to
     // nearest even of x / descale, saturating at +-448, NaN to 0x7F; the same encoder),

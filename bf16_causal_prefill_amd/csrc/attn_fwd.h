@@ -711,18 +711,14 @@ void attn_fwd_kernel(FwdParams p) {
     const bool masked = t * BN + BN - 1 > w_lim;
     if (masked) {
       // element i of M-tile m holds key t*BN + 32m + 4g + off_i, off_i = 8(i/4) + i%4;
-      // it is masked when off_i > d_m = lim - (t*BN + 32m + 4g), lim = the row's last
-      // visible key.  Select with integer ops (sign of d_m - off_i) rather than
-      // per-element lane-mask compares.
+      // it is masked when 32m + off_i > d0 = lim - (t*BN + 4g), lim = the row's last
+      // visible key: one compare of d0 with a constant per element.
       const int d0 = min(q0w + l32 + q_off, Nk - 1) - (t * BN + 4 * g);
 #pragma unroll
       for (int m = 0; m < C::MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int keep = (d0 - 32 * m - (8 * (i >> 2) + (i & 3))) >> 31;   // -1: masked
-          const uint32_t bits = __float_as_uint(s[m][i]);
-          s[m][i] = __uint_as_float((bits & ~(uint32_t)keep) | (0xff800000u & (uint32_t)keep));
-        }
+        for (int i = 0; i < 16; ++i)
+          s[m][i] = d0 < 32 * m + 8 * (i >> 2) + (i & 3) ? -INFINITY : s[m][i];
     }
     if (masked || !MAX_IN_MFMA) {
       // max over each 64-key block (this lane's 32 keys, then the other lane half's)

@@ -931,8 +931,8 @@ void attn_fwd_kernel(FwdParams p) {
   // holds the registers of its own softmax path only (a loop wrapped in a lambda spills,
   // hence the macro).
   // The pipeline's fill (t = 0: Q K^T only, while group B waits at its extra barrier) and
-  // drain (t = n_kt: P V only, group B alone at the end) run outside the loop with only
-  // the slots they need (measured +2.4-3.3% at 4K, +1.1-1.3% at mla32k, outputs
+  // drain (t = n_kt: P V only; group B's comes after group A has finished) run outside the
+  // loop with only the slots they need (measured +2.4-3.3% at 4K, +1.1-1.3% at mla32k, outputs
   // unchanged).  Peeling the fill puts a second copy of the softmax phase outside the
   // loop; in the two exact-LSE kernels nearest the 256-VGPR limit (the exact channels,
   // and d192 with float32 Q) that made the register allocator spill, so they keep the
